@@ -1,0 +1,220 @@
+"""Python binding of the gfx950 low-bit MLA cache library (libmla_lowbit.so).
+
+Thin argument marshalling over the C ABI declared in include/mla_lowbit.h:
+every entry point keeps its C name, takes torch tensors that already live on
+the GPU, checks their dtype/shape/device, and passes raw device pointers and
+the current HIP stream.  All computation happens in the library's HIP
+kernels; there is no fallback path: if the library is missing or the tensors
+are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FORMATS", "MlaError", "format_struct", "load_library",
+    "mla_token_bytes", "mla_page_bytes", "mla_quant_append", "mla_decode_num_splits",
+    "mla_decode_workspace_bytes", "mla_decode_lowbit", "mla_decode_partial", "mla_decode_combine",
+    "mla_last_error", "alloc_cache",
+]
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_lowbit.so")
+
+# name -> (c_bits, c_group, r_bits, r_group, d_c, d_r, page_size)
+FORMATS = {
+    "C4R4": (4, 64, 4, 64, 512, 64, 64),
+    "C2R4": (2, 32, 4, 64, 512, 64, 64),
+    "BF16": (16, 0, 16, 0, 512, 64, 64),
+}
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+_STATUS = {1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), msg))
+        self.status = status
+
+
+class mla_format_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("c_bits", "c_group", "r_bits", "r_group", "d_c", "d_r", "page_size")]
+
+
+def format_struct(fmt) -> mla_format_t:
+    """mla_format_t from a name ("C4R4", "C2R4", "BF16") or a 7-tuple."""
+    vals = FORMATS[fmt] if isinstance(fmt, str) else tuple(int(v) for v in fmt)
+    return mla_format_t(*vals)
+
+
+_lib = None
+
+
+def load_library():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libmla_lowbit.so is not built (run __graft_entry__.build()); "
+                           "there is no fallback implementation")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    FP = ctypes.POINTER(mla_format_t)
+    sig = {
+        "mla_token_bytes": (SZ, [FP]),
+        "mla_page_bytes": (SZ, [FP]),
+        "mla_quant_append": (ctypes.c_int, [FP, P, P, P, I32, P, I64, P]),
+        "mla_decode_num_splits": (I32, [FP, I32, I32, I32]),
+        "mla_decode_workspace_bytes": (SZ, [FP, I32, I32, I32]),
+        "mla_decode_lowbit": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P, P, P]),
+        "mla_decode_partial": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P]),
+        "mla_decode_combine": (ctypes.c_int, [FP, I32, I32, I32, P, SZ, P, P, P]),
+        "mla_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def mla_last_error() -> str:
+    return load_library().mla_last_error().decode()
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MlaError(status, mla_last_error())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, name, dtype=None):
+    return ctypes.c_void_p(0) if t is None else _dev(t, name, dtype)
+
+
+# ---------------------------------------------------------------------- entry points
+
+def mla_token_bytes(fmt) -> int:
+    return int(load_library().mla_token_bytes(ctypes.byref(format_struct(fmt))))
+
+
+def mla_page_bytes(fmt) -> int:
+    return int(load_library().mla_page_bytes(ctypes.byref(format_struct(fmt))))
+
+
+def alloc_cache(fmt, num_pages: int, device="cuda"):
+    """Zeroed paged cache: uint8 [num_pages * page_bytes] on `device`."""
+    import torch
+    return torch.zeros(num_pages * mla_page_bytes(fmt), dtype=torch.uint8, device=device)
+
+
+def mla_quant_append(fmt, latent, rope, slot_mapping, cache, num_pages=None, stream=None) -> None:
+    """Quantize and pack bf16 rows latent [n, 512] / rope [n, 64] into `cache` at `slot_mapping` [n] int32."""
+    import torch
+    n = int(latent.shape[0]) if latent.dim() == 2 else -1
+    if latent.dim() != 2 or rope.dim() != 2 or rope.shape[0] != n or slot_mapping.shape != (n,):
+        raise ValueError("latent [n, 512], rope [n, 64] and slot_mapping [n] expected")
+    pb = mla_page_bytes(fmt)
+    if num_pages is None:
+        num_pages = cache.numel() // pb if pb else 0
+    if pb and cache.numel() < num_pages * pb:
+        raise ValueError("cache holds fewer than num_pages pages")
+    _check(load_library().mla_quant_append(
+        ctypes.byref(format_struct(fmt)), _dev(latent, "latent", torch.bfloat16), _dev(rope, "rope", torch.bfloat16),
+        _dev(slot_mapping, "slot_mapping", torch.int32), n, _dev(cache, "cache", torch.uint8), int(num_pages),
+        _stream(stream)))
+
+
+def mla_decode_num_splits(fmt, batch: int, num_heads: int, max_seq_len: int) -> int:
+    return int(load_library().mla_decode_num_splits(ctypes.byref(format_struct(fmt)), batch, num_heads, max_seq_len))
+
+
+def mla_decode_workspace_bytes(fmt, batch: int, num_heads: int, num_splits: int) -> int:
+    return int(load_library().mla_decode_workspace_bytes(ctypes.byref(format_struct(fmt)), batch, num_heads,
+                                                         num_splits))
+
+
+def _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages):
+    if q.dim() != 3 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("q [B, H, 576], block_table [B, max_pages] and seq_lens [B] expected")
+    B, H, D = (int(v) for v in q.shape)
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("batch sizes of q, block_table and seq_lens differ")
+    pb = mla_page_bytes(fmt)
+    if num_pages is None:
+        num_pages = cache.numel() // pb if pb else 0
+    return B, H, int(block_table.shape[1]), int(num_pages)
+
+
+def mla_decode_lowbit(fmt, q, cache, block_table, seq_lens, softmax_scale, max_seq_len=None, num_splits=0,
+                      out=None, lse=None, workspace=None, num_pages=None, stream=None):
+    """Decode attention over the packed cache; returns (out bf16 [B, H, 512], lse fp32 [B, H] or None).
+
+    `max_seq_len` is the host-side bound on seq_lens used to choose splits (default: capacity)."""
+    import torch
+    B, H, MP, NP = _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
+    if max_seq_len is None:
+        max_seq_len = MP * 64
+    S = num_splits or mla_decode_num_splits(fmt, B, H, max_seq_len)
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    ws_bytes = mla_decode_workspace_bytes(fmt, B, H, S) if S > 1 else 0
+    if workspace is None and S > 1:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check(load_library().mla_decode_lowbit(
+        ctypes.byref(format_struct(fmt)), _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.uint8), NP,
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
+        int(max_seq_len), float(softmax_scale), int(num_splits),
+        _opt(workspace, "workspace", torch.uint8), workspace.numel() if workspace is not None else 0,
+        _dev(out, "out", torch.bfloat16), _opt(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse
+
+
+def mla_decode_partial(fmt, q, cache, block_table, seq_lens, softmax_scale, num_splits, workspace,
+                       max_seq_len=None, num_pages=None, stream=None) -> None:
+    import torch
+    B, H, MP, NP = _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
+    if max_seq_len is None:
+        max_seq_len = MP * 64
+    _check(load_library().mla_decode_partial(
+        ctypes.byref(format_struct(fmt)), _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.uint8), NP,
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
+        int(max_seq_len), float(softmax_scale), int(num_splits), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream)))
+
+
+def mla_decode_combine(fmt, batch, num_heads, num_splits, workspace, out, lse=None, stream=None) -> None:
+    import torch
+    _check(load_library().mla_decode_combine(
+        ctypes.byref(format_struct(fmt)), int(batch), int(num_heads), int(num_splits),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _dev(out, "out", torch.bfloat16),
+        _opt(lse, "lse", torch.float32), _stream(stream)))
+
+
+def workspace_views(fmt, workspace, batch, num_heads, num_splits):
+    """fp32 views (o_part [B, S, H, 512], lse_part [B, S, H]) of a decode workspace."""
+    import torch
+    n_o = batch * num_splits * num_heads * 512
+    o_bytes = (n_o * 4 + 255) // 256 * 256
+    o = workspace[:n_o * 4].view(torch.float32).view(batch, num_splits, num_heads, 512)
+    l = workspace[o_bytes:o_bytes + batch * num_splits * num_heads * 4].view(torch.float32)
+    return o, l.view(batch, num_splits, num_heads)

@@ -1,0 +1,240 @@
+// C ABI of the gfx950 low-bit MLA cache library: argument validation, split
+// selection, workspace layout and kernel launches.  See include/mla_lowbit.h
+// for the contract of every entry point.
+#include "mla_lowbit.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status_t fail(mla_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// Compute units of one MI355X; the split heuristic aims at whole waves of
+// one workgroup per compute unit.
+constexpr int kComputeUnits = 256;
+constexpr int kMaxSplits = 64;
+constexpr int kMaxPagesPerSplit = 128;
+
+int format_id(const mla_format_t* f) {
+  if (!f) return -1;
+  if (f->d_c != mla::kDc || f->d_r != mla::kDr || f->page_size != mla::kPage) return -1;
+  if (f->c_bits == 4 && f->c_group == 64 && f->r_bits == 4 && f->r_group == 64) return mla::kC4R4;
+  if (f->c_bits == 2 && f->c_group == 32 && f->r_bits == 4 && f->r_group == 64) return mla::kC2R4;
+  if (f->c_bits == 16 && f->r_bits == 16) return mla::kBF16;
+  return -1;
+}
+
+size_t page_bytes_of(int id) {
+  switch (id) {
+    case mla::kC4R4: return mla::PageLayout<mla::kC4R4>::kBytes;
+    case mla::kC2R4: return mla::PageLayout<mla::kC2R4>::kBytes;
+    case mla::kBF16: return mla::PageLayout<mla::kBF16>::kBytes;
+    default: return 0;
+  }
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t partial_o_bytes(int batch, int heads, int splits) {
+  return align_up((size_t)batch * splits * heads * mla::kDc * sizeof(float), 256);
+}
+
+size_t workspace_bytes(int batch, int heads, int splits) {
+  return partial_o_bytes(batch, heads, splits) + align_up((size_t)batch * splits * heads * sizeof(float), 256);
+}
+
+int auto_splits(int batch, int max_seq_len) {
+  const int pages = (max_seq_len + mla::kPage - 1) / mla::kPage;
+  if (batch <= 0 || pages <= 1) return 1;
+  int s = (kComputeUnits + batch - 1) / batch;                       // fill the compute units
+  const int s_len = (pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;  // bound the longest split
+  if (s_len > s) s = s_len;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > pages) s = pages;
+  return s < 1 ? 1 : s;
+}
+
+struct DecodeShape {
+  int fmt;
+  int splits;
+  int pages_per_split;
+};
+
+mla_status_t check_decode(const mla_format_t* fmt, const void* q, const void* cache, int64_t num_pages,
+                          const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                          int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                          DecodeShape* shape) {
+  shape->fmt = format_id(fmt);
+  if (shape->fmt < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  if (batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch above 65535 is not supported (got %d)", batch);
+  if (num_heads < 1 || num_heads > 128)
+    return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128 (got %d)", num_heads);
+  if (max_pages_per_seq < 1) return fail(MLA_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (max_seq_len < 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_INVALID_ARG, "num_splits must be in 0..%d (got %d)", kMaxSplits, num_splits);
+  if (batch > 0) {
+    if (!q || !cache || !block_table || !seq_lens) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(q, 16) || !aligned(cache, 16))
+      return fail(MLA_ERR_INVALID_ARG, "q and cache must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+      return fail(MLA_ERR_INVALID_ARG, "block_table and seq_lens must be 4-byte aligned");
+  }
+  int64_t cap = (int64_t)max_pages_per_seq * mla::kPage;
+  int64_t hint = max_seq_len < cap ? max_seq_len : cap;
+  shape->splits = num_splits > 0 ? num_splits : auto_splits(batch, (int)hint);
+  const int pages = (int)((hint + mla::kPage - 1) / mla::kPage);
+  int pps = (pages + shape->splits - 1) / shape->splits;
+  shape->pages_per_split = pps < 1 ? 1 : pps;
+  return MLA_OK;
+}
+
+mla::DecodeArgs make_args(const void* q, const void* cache, int64_t num_pages, const int32_t* block_table,
+                          const int32_t* seq_lens, int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
+                          float softmax_scale, const DecodeShape& sh, void* workspace) {
+  mla::DecodeArgs a{};
+  a.q = (const __bf16*)q;
+  a.cache = (const uint8_t*)cache;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.heads = num_heads;
+  a.max_pages = max_pages_per_seq;
+  a.num_splits = sh.splits;
+  a.pages_per_split = sh.pages_per_split;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  if (workspace) {
+    a.o_part = (float*)workspace;
+    a.lse_part = (float*)((char*)workspace + partial_o_bytes(batch, num_heads, sh.splits));
+  }
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_token_bytes(const mla_format_t* fmt) { return page_bytes_of(format_id(fmt)) / mla::kPage; }
+
+size_t mla_page_bytes(const mla_format_t* fmt) { return page_bytes_of(format_id(fmt)); }
+
+const char* mla_last_error(void) { return g_err; }
+
+mla_status_t mla_quant_append(const mla_format_t* fmt, const void* latent_bf16, const void* rope_bf16,
+                              const int32_t* slot_mapping, int32_t n_new, void* cache, int64_t num_pages,
+                              void* stream) {
+  const int id = format_id(fmt);
+  if (id < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
+  if (n_new < 0) return fail(MLA_ERR_INVALID_ARG, "n_new must be >= 0 (got %d)", n_new);
+  if (n_new == 0) return MLA_OK;
+  if (!latent_bf16 || !rope_bf16 || !slot_mapping || !cache) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (!aligned(latent_bf16, 16) || !aligned(rope_bf16, 16) || !aligned(cache, 16))
+    return fail(MLA_ERR_INVALID_ARG, "latent, rope and cache must be 16-byte aligned");
+  if (!aligned(slot_mapping, 4)) return fail(MLA_ERR_INVALID_ARG, "slot_mapping must be 4-byte aligned");
+  hipError_t e = mla::launch_quant_append(id, latent_bf16, rope_bf16, slot_mapping, n_new, cache, num_pages,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "quant_append launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t max_seq_len) {
+  (void)fmt;
+  (void)num_heads;
+  return auto_splits(batch, max_seq_len);
+}
+
+size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits) {
+  if (format_id(fmt) < 0 || batch < 0 || num_heads < 1 || num_splits < 1) return 0;
+  return workspace_bytes(batch, num_heads, num_splits);
+}
+
+mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,
+                                const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
+                                float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  DecodeShape sh;
+  mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                 max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
+  if (st != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (!workspace || !aligned(workspace, 256))
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+  if (ws_bytes < workspace_bytes(batch, num_heads, sh.splits))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                workspace_bytes(batch, num_heads, sh.splits));
+  mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                max_pages_per_seq, softmax_scale, sh, workspace);
+  hipError_t e = mla::launch_decode(sh.fmt, false, a, batch, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits,
+                                const void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out,
+                                void* stream) {
+  if (format_id(fmt) < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
+  if (batch < 0 || batch > 65535) return fail(MLA_ERR_INVALID_ARG, "batch must be in 0..65535");
+  if (num_heads < 1 || num_heads > 128) return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128");
+  if (num_splits < 1 || num_splits > kMaxSplits) return fail(MLA_ERR_INVALID_ARG, "num_splits must be in 1..64");
+  if (batch == 0) return MLA_OK;
+  if (!workspace || !out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(workspace, 256) || !aligned(out_bf16, 16) || (lse_out && !aligned(lse_out, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "misaligned workspace or output");
+  if (ws_bytes < workspace_bytes(batch, num_heads, num_splits))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                workspace_bytes(batch, num_heads, num_splits));
+  const float* o_part = (const float*)workspace;
+  const float* lse_part = (const float*)((const char*)workspace + partial_o_bytes(batch, num_heads, num_splits));
+  hipError_t e = mla::launch_combine(o_part, lse_part, batch, num_heads, num_splits, (__bf16*)out_bf16, lse_out,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,
+                               const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                               int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
+                               float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
+                               void* out_bf16, float* lse_out, void* stream) {
+  DecodeShape sh;
+  mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                 max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
+  if (st != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MLA_ERR_INVALID_ARG, "out must be a 16-byte aligned pointer");
+  if (lse_out && !aligned(lse_out, 4)) return fail(MLA_ERR_INVALID_ARG, "lse_out must be 4-byte aligned");
+  if (sh.splits == 1) {
+    mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                  max_pages_per_seq, softmax_scale, sh, nullptr);
+    a.out = (__bf16*)out_bf16;
+    a.lse_out = lse_out;
+    hipError_t e = mla::launch_decode(sh.fmt, true, a, batch, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return MLA_OK;
+  }
+  st = mla_decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+                          max_seq_len, softmax_scale, sh.splits, workspace, ws_bytes, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_combine(fmt, batch, num_heads, sh.splits, workspace, ws_bytes, out_bf16, lse_out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,517 @@
+// Split-KV decode attention over the paged low-bit MLA cache (gfx950).
+//
+// Math (absorbed MLA decode; QuantMLA's low-bit kernel unpacks and
+// dequantizes the cache inside attention -- "QuantMLA: INT4 (and INT2) for
+// both halves of the MLA cache", flowchart and Key findings, systems):
+//   S[h, t] = scale * <q[h, 0:576], khat[t, 0:576]>       (latent + RoPE key)
+//   O[h, :] = sum_t softmax_t(S[h, :]) * khat[t, 0:512]   (latent is the value)
+//
+// One workgroup = one (split, sequence) pair, 256 threads = 4 wavefronts, one
+// per SIMD.  Wave w owns heads [32w, 32w + 32).  The work is tiled by half
+// pages (32 tokens):
+//   1. fill: every thread loads its share of the next tile's packed bytes
+//      (16-byte loads; the 32 lanes of a half-wave read 512 contiguous bytes of
+//      one code chunk), dequantizes them in registers once for all heads
+//      (bf16(fma(code, S, Z))) and writes a bf16 tile khat[32][576] to LDS
+//      (rows padded to 1168 bytes).  Tiles are double
+//      buffered, so the loads of tile k+1 are in flight while tile k computes.
+//   2. Q.K^T on MFMA 32x32x16 bf16: A = khat rows (ds_read_b128), B = q^T held
+//      in registers for the whole split (32 heads x 576 = 144 VGPRs), giving
+//      S^T[token][head]: each lane holds one head and 16 tokens per block.
+//   3. softmax weights in registers: per-head max over the lane's tokens, the
+//      other half-wave via v_permlane32_swap; exp2 with the scale folded into
+//      log2 units.  Weights are taken against a fixed reference per split (the
+//      first tile's max), so O is never rescaled and stays in the MFMA
+//      accumulators; a split whose logits rise more than 2^64 above that
+//      reference is recomputed with its true max (see split_pass).
+//   4. P.V on MFMA 32x32x16 bf16 with the latent as value: A = khat^T read
+//      with ds_read_b64_tr_b16 (transposing 16-bit loads) from the same tile,
+//      B = P straight from the softmax registers.  P is split into a bf16 high
+//      part and a bf16 remainder (two MFMAs sharing A) so the weights keep
+//      ~16 significant bits; a single bf16 P loses too much accuracy when a few
+//      tokens with large, cancelling latent values dominate a head.
+//      O^T[channel][head] accumulates in 256 fp32 registers per lane.
+//   5. per split: O / l and lse = m + log l are written as fp32 partials (or,
+//      with one split, the final bf16 output directly).
+// A second kernel merges the splits with log-sum-exp weights.
+#include "kernels.h"
+
+namespace mla {
+
+constexpr int kTileTok = 32;                // tokens per tile (half a page)
+constexpr int kRow = kD + 8;                // LDS row stride in bf16: 1168 B
+constexpr int kTile = kTileTok * kRow;      // elements per tile buffer (40 KB)
+constexpr int kThreads = 256;
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// LDS tile: row r (token) at r * 1168 bytes, 16-byte chunk c (channels
+// 8c .. 8c + 7) at byte 16 c.  1168 = 144 (mod 256), so 16 consecutive rows
+// reading the same chunk hit distinct banks.  Addresses stay affine in the
+// loop indices, so they fold into instruction offsets.
+__device__ __forceinline__ int tile_off(int r, int chunk) { return r * kRow + 8 * chunk; }
+
+__device__ __forceinline__ float wave_partner(float v) {
+  // value of lane l ^ 32
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                            false, false);
+  const unsigned other = (threadIdx.x & 32) ? r[0] : r[1];
+  return __builtin_bit_cast(float, other);
+}
+
+// ---------------------------------------------------------------- dequantization
+
+// 8 INT4 codes of one dword (element e at bits 4e) -> 8 bf16 values.
+__device__ __forceinline__ bf16x8 dq_int4(unsigned w, float S, float Z) {
+  const unsigned lo = w & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const unsigned hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = __builtin_fmaf((float)((lo >> (8 * k)) & 0xFFu), S, Z);
+    const float b = __builtin_fmaf((float)((hi >> (8 * k)) & 0xFFu), S, Z);
+    r[k] = pack_bf16x2(a, b);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 16 INT2 codes of one dword (element e at bits 2e), all of one group -> 16 bf16 values.
+__device__ __forceinline__ void dq_int2(unsigned w, float S, float Z, bf16x8& o0, bf16x8& o1) {
+  // byte k of (w >> 2j) & 0x03030303 holds element 4k + j
+  const unsigned b0 = w & 0x03030303u, b1 = (w >> 2) & 0x03030303u;
+  const unsigned b2 = (w >> 4) & 0x03030303u, b3 = (w >> 6) & 0x03030303u;
+  u32x4 r0, r1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float e0 = __builtin_fmaf((float)((b0 >> (8 * k)) & 0xFFu), S, Z);
+    const float e1 = __builtin_fmaf((float)((b1 >> (8 * k)) & 0xFFu), S, Z);
+    const float e2 = __builtin_fmaf((float)((b2 >> (8 * k)) & 0xFFu), S, Z);
+    const float e3 = __builtin_fmaf((float)((b3 >> (8 * k)) & 0xFFu), S, Z);
+    const unsigned p01 = pack_bf16x2(e0, e1), p23 = pack_bf16x2(e2, e3);
+    if (k < 2) { r0[2 * k] = p01; r0[2 * k + 1] = p23; }
+    else { r1[2 * (k - 2)] = p01; r1[2 * (k - 2) + 1] = p23; }
+  }
+  o0 = __builtin_bit_cast(bf16x8, r0);
+  o1 = __builtin_bit_cast(bf16x8, r1);
+}
+
+__device__ __forceinline__ void sz_unpack(unsigned sz, float& S, float& Z) {
+  S = half_bits_to_f32(sz);
+  Z = half_bits_to_f32(sz >> 16);
+}
+
+// ---------------------------------------------------------------- tile fills
+// A tile is half a page: tokens [32 hp, 32 hp + 32) of one physical page.
+// Thread mapping: t = tid % 32 is the token, cs = tid / 32 selects chunks, so
+// the 32 lanes of a half-wave read 512 contiguous bytes of one code chunk.
+// load(page, hp): issue this thread's global loads into registers.
+// store(tile, nvalid): dequantize into the LDS tile; rows >= nvalid are zero.
+
+template <int F> struct Fill;
+
+template <> struct Fill<kC4R4> {
+  using Lay = PageLayout<kC4R4>;
+  u32x4 c[2];
+  unsigned sz[2];
+  u32x4 r;
+  unsigned rsz;
+  bool ok;
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
+    const int t = (threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+    ok = page >= 0 && page < num_pages;
+    const uint8_t* base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = cs + 8 * i;  // content chunk = channels [32j, 32j + 32), group j / 2
+      c[i] = *(const u32x4*)(base + Lay::kCodesA + (j * kPage + t) * 16);
+      sz[i] = *(const unsigned*)(base + Lay::kSzB + ((j >> 1) * kPage + t) * 4);
+    }
+    if (cs < 2) {
+      r = *(const u32x4*)(base + Lay::kCodesC + (cs * kPage + t) * 16);
+      rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* tile, int nvalid) const {
+    const int t = threadIdx.x & 31, cs = threadIdx.x >> 5;
+    const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = cs + 8 * i;
+      float S, Z;
+      sz_unpack(live ? sz[i] : 0u, S, Z);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *(bf16x8*)(tile + tile_off(t, 4 * j + v)) = dq_int4(live ? c[i][v] : 0u, S, Z);
+    }
+    if (cs < 2) {
+      float S, Z;
+      sz_unpack(live ? rsz : 0u, S, Z);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *(bf16x8*)(tile + tile_off(t, 64 + 4 * cs + v)) = dq_int4(live ? r[v] : 0u, S, Z);
+    }
+  }
+};
+
+template <> struct Fill<kC2R4> {
+  using Lay = PageLayout<kC2R4>;
+  u32x4 c;
+  unsigned sz[2];
+  u32x4 r;
+  unsigned rsz;
+  bool ok;
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
+    const int t = (threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+    ok = page >= 0 && page < num_pages;
+    const uint8_t* base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
+    // content chunk cs = channels [64 cs, 64 cs + 64) = groups 2 cs, 2 cs + 1
+    c = *(const u32x4*)(base + Lay::kCodesA + (cs * kPage + t) * 16);
+    sz[0] = *(const unsigned*)(base + Lay::kSzB + ((2 * cs) * kPage + t) * 4);
+    sz[1] = *(const unsigned*)(base + Lay::kSzB + ((2 * cs + 1) * kPage + t) * 4);
+    if (cs < 2) {
+      r = *(const u32x4*)(base + Lay::kCodesC + (cs * kPage + t) * 16);
+      rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* tile, int nvalid) const {
+    const int t = threadIdx.x & 31, cs = threadIdx.x >> 5;
+    const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      // dword v = channels [64 cs + 16 v, +16), group 2 cs + v / 2
+      float S, Z;
+      sz_unpack(live ? sz[v >> 1] : 0u, S, Z);
+      bf16x8 x0, x1;
+      dq_int2(live ? c[v] : 0u, S, Z, x0, x1);
+      *(bf16x8*)(tile + tile_off(t, 8 * cs + 2 * v)) = x0;
+      *(bf16x8*)(tile + tile_off(t, 8 * cs + 2 * v + 1)) = x1;
+    }
+    if (cs < 2) {
+      float S, Z;
+      sz_unpack(live ? rsz : 0u, S, Z);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *(bf16x8*)(tile + tile_off(t, 64 + 4 * cs + v)) = dq_int4(live ? r[v] : 0u, S, Z);
+    }
+  }
+};
+
+// Unquantized baseline: 32 rows x 72 chunks of 16 bytes, copied through
+// registers (nine chunks per thread, in three rounds) at store time.  Rows of
+// the page past the sequence end are read (they are inside the page) and
+// replaced by zeros.
+template <> struct Fill<kBF16> {
+  const uint8_t* base;
+  bool ok;
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
+    ok = page >= 0 && page < num_pages;
+    base = cache + (ok ? page : 0) * (int64_t)PageLayout<kBF16>::kBytes + hp * (kTileTok * kD * 2);
+  }
+  __device__ __forceinline__ void store(__bf16* tile, int nvalid) const {
+#pragma unroll
+    for (int round = 0; round < 3; ++round) {
+      u32x4 v[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) v[i] = *(const u32x4*)(base + (threadIdx.x + kThreads * (3 * round + i)) * 16);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int ci = threadIdx.x + kThreads * (3 * round + i);  // 0 .. 2303
+        const int t = ci / 72, col = ci % 72;
+        const bool live = ok && t < nvalid;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *(u32x4*)(tile + tile_off(t, col)) = live ? v[i] : z;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- decode kernel
+
+// Result of one pass over a split, per lane: O^T accumulators (channels x the
+// lane's head), softmax denominator part and reference.
+struct SplitAcc {
+  f32x16 o[16];
+  float l_sum;   // this lane's share of sum_t p_t
+  float m_ref;   // reference (log2 units) the p_t are taken against
+  float m_seen;  // true max logit of the head over the split (log2 units)
+};
+
+// Softmax weights are taken against a fixed reference per split: the first
+// tile's max (pass 1), so O never needs rescaling and stays in MFMA
+// accumulators.  Later tiles may exceed it; p = 2^(x - m_ref) is allowed up to
+// 2^kMaxLift, which keeps l and O far inside the fp32 range.  If any logit of
+// the split lies more than kMaxLift above the reference, the pass reports it
+// and the caller recomputes the split with m_ref = the split's true max.
+constexpr float kMaxLift = 64.0f;
+
+template <int F>
+__device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int k0,
+                                           int k1, const bf16x8 (&qr)[36], bool fixed, float m_fixed,
+                                           SplitAcc& acc) {
+  const int lane = threadIdx.x & 63, hi = lane >> 5;
+  // transposing-read addresses for the P.V operand: lane (g, i) = (lane / 16,
+  // lane % 16) reads 4 channels of one token row; see the kernel comment.
+  const int g = lane >> 4, i16 = lane & 15;
+  const int tr_row0 = 4 * (g >> 1) + (i16 >> 2);        // token quad 0 or 1 of a 16-token step
+  const int tr_chunk = 2 * (g & 1) + ((i16 & 3) >> 1);   // + 4 ct
+  const int tr_half = 4 * (i16 & 1);
+
+#pragma unroll
+  for (int ct = 0; ct < 16; ++ct) acc.o[ct] = (f32x16){};
+  acc.l_sum = 0.0f;
+  acc.m_ref = fixed ? m_fixed : -INFINITY;
+  acc.m_seen = -INFINITY;
+  bool lifted = false;
+
+  Fill<F> fill;
+  fill.load(a.cache, bt[k0 >> 1], k0 & 1, a.num_pages);
+  fill.store(smem, min(kTileTok, L - k0 * kTileTok));
+  __syncthreads();
+
+  for (int k = k0; k < k1; ++k) {
+    __bf16* tile = smem + ((k - k0) & 1) * kTile;
+    __bf16* next = smem + ((k - k0 + 1) & 1) * kTile;
+    const bool more = k + 1 < k1;
+    if (more) fill.load(a.cache, bt[(k + 1) >> 1], (k + 1) & 1, a.num_pages);
+
+    const int nvalid = min(kTileTok, L - k * kTileTok);
+    // ---- S^T = khat . q^T for the 32 tokens of the tile
+    f32x16 s = {};
+    const int arow = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+      const bf16x8 kv = *(const bf16x8*)(tile + tile_off(arow, 2 * ks + hi));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qr[ks], s, 0, 0, 0);
+    }
+    // ---- softmax weights (log2 domain); reg r is token 8 (r / 4) + 4 hi + r % 4
+    float x[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t0 = 8 * (r >> 2) + 4 * hi + (r & 3);
+      x[r] = t0 < nvalid ? s[r] * a.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, x[r]);
+    }
+    mt = fmaxf(mt, wave_partner(mt));
+    acc.m_seen = fmaxf(acc.m_seen, mt);
+    if (k == k0 && !fixed) acc.m_ref = mt;
+    lifted |= mt - acc.m_ref > kMaxLift;
+    float ps = 0.0f;
+    unsigned phi[8], plo[8];  // packed bf16 pairs: P high part and remainder
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float pa = exp2f(fminf(x[r] - acc.m_ref, kMaxLift));
+      const float pb = exp2f(fminf(x[r + 1] - acc.m_ref, kMaxLift));
+      ps += pa + pb;
+      const unsigned h2 = pack_bf16x2(pa, pb);
+      phi[r >> 1] = h2;
+      plo[r >> 1] = pack_bf16x2(pa - bf16_lo(h2), pb - bf16_hi(h2));
+    }
+    acc.l_sum += ps;
+    // ---- O^T += khat^T . P  (k-step kk covers tile tokens 16 kk .. 16 kk + 15)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, (u32x4){phi[4 * kk], phi[4 * kk + 1], phi[4 * kk + 2], phi[4 * kk + 3]});
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, (u32x4){plo[4 * kk], plo[4 * kk + 1], plo[4 * kk + 2], plo[4 * kk + 3]});
+      const __bf16* v0 = tile + (16 * kk + tr_row0) * kRow + 8 * tr_chunk + tr_half;
+      const __bf16* v1 = v0 + 8 * kRow;
+#pragma unroll
+      for (int ct = 0; ct < 16; ++ct) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + 32 * ct));
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v1 + 32 * ct));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bh, acc.o[ct], 0, 0, 0);
+        acc.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bl, acc.o[ct], 0, 0, 0);
+      }
+    }
+    if (more) fill.store(next, min(kTileTok, L - (k + 1) * kTileTok));
+    __syncthreads();
+  }
+  return lifted;
+}
+
+// The same tile sequence for a wavefront that owns no heads (num_heads below
+// 32 w): it only helps fill the tiles and keeps the barrier sequence.
+template <int F>
+__device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L,
+                                                     int k0, int k1) {
+  Fill<F> fill;
+  fill.load(a.cache, bt[k0 >> 1], k0 & 1, a.num_pages);
+  fill.store(smem, min(kTileTok, L - k0 * kTileTok));
+  __syncthreads();
+  for (int k = k0; k < k1; ++k) {
+    __bf16* next = smem + ((k - k0 + 1) & 1) * kTile;
+    if (k + 1 < k1) {
+      fill.load(a.cache, bt[(k + 1) >> 1], (k + 1) & 1, a.num_pages);
+      fill.store(next, min(kTileTok, L - (k + 1) * kTileTok));
+    }
+    __syncthreads();
+  }
+}
+
+template <bool kDirect>
+__device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int split, int head, const SplitAcc& acc) {
+  const int hi = (threadIdx.x & 63) >> 5;
+  const float l_tot = acc.l_sum + wave_partner(acc.l_sum);
+  const float inv = 1.0f / l_tot;
+  const float lse = (acc.m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+  const int H = a.heads;
+  if (head >= H) return;
+  if (kDirect) {
+    __bf16* orow = a.out + ((int64_t)b * H + head) * kDc + 4 * hi;
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const unsigned w0 = pack_bf16x2(acc.o[ct][4 * rq] * inv, acc.o[ct][4 * rq + 1] * inv);
+        const unsigned w1 = pack_bf16x2(acc.o[ct][4 * rq + 2] * inv, acc.o[ct][4 * rq + 3] * inv);
+        *(uint2*)(orow + 32 * ct + 8 * rq) = make_uint2(w0, w1);
+      }
+    if (a.lse_out && hi == 0) a.lse_out[b * H + head] = lse;
+  } else {
+    const int64_t row = ((int64_t)b * a.num_splits + split) * H + head;
+    float* orow = a.o_part + row * kDc + 4 * hi;
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x4 v = {acc.o[ct][4 * rq] * inv, acc.o[ct][4 * rq + 1] * inv, acc.o[ct][4 * rq + 2] * inv,
+                         acc.o[ct][4 * rq + 3] * inv};
+        *(f32x4*)(orow + 32 * ct + 8 * rq) = v;
+      }
+    if (hi == 0) a.lse_part[row] = lse;
+  }
+}
+
+template <int F, bool kDirect>
+__global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int H = a.heads;
+
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
+  const int n_pages = (L + kPage - 1) / kPage;
+  const int p0 = split * a.pages_per_split;
+  const int p1 = (split == a.num_splits - 1) ? n_pages : min(p0 + a.pages_per_split, n_pages);
+
+  if (p0 >= p1) {  // empty split
+    if (kDirect) {
+      for (int i = tid; i < H * kDc; i += kThreads) a.out[(int64_t)b * H * kDc + i] = (__bf16)0.0f;
+      if (a.lse_out && tid < H) a.lse_out[b * H + tid] = -INFINITY;
+    } else if (tid < H) {
+      a.lse_part[((int64_t)b * a.num_splits + split) * H + tid] = -INFINITY;
+    }
+    return;
+  }
+  // tiles are half pages: tile k covers tokens [32 k, 32 k + 32)
+  const int k0 = 2 * p0;
+  const int k1 = min(2 * p1, (L + kTileTok - 1) / kTileTok);
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+
+  if (wave * 32 >= H) {  // no heads for this wavefront: fill only (uniform per wave)
+    for (int pass = 0;; ++pass) {
+      split_pass_fill_only<F>(a, smem, bt, L, k0, k1);
+      const bool redo = __syncthreads_or(0);
+      if (!redo || pass > 0) return;
+    }
+  }
+
+  const int head = wave * 32 + (lane & 31);
+  const int hi = lane >> 5;
+  // q^T operand: lane holds head `head`, channels 16 ks + 8 hi + [0, 8)
+  bf16x8 qr[36];
+  {
+    const int hq = head < H ? head : H - 1;
+    const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi;
+    const bf16x8 zero = {};
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+      const bf16x8 v = *(const bf16x8*)(qh + 16 * ks);
+      qr[ks] = head < H ? v : zero;
+    }
+  }
+  // pass 0 takes the first tile's max as reference; a second pass (rare) uses
+  // the split's true max found by pass 0.
+  bool fixed = false;
+  float m_fixed = 0.0f;
+  for (int pass = 0;; ++pass) {
+    SplitAcc acc;
+    const bool lifted = split_pass<F>(a, smem, bt, L, k0, k1, qr, fixed, m_fixed, acc);
+    const bool redo = __syncthreads_or(lifted);
+    if (!redo || pass > 0) {
+      write_split<kDirect>(a, b, split, head, acc);
+      return;
+    }
+    fixed = true;
+    m_fixed = acc.m_seen;
+  }
+}
+
+// ---------------------------------------------------------------- combine kernel
+// One wavefront per (sequence, head): lane owns channels [8 lane, 8 lane + 8).
+// out = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse); empty splits
+// (lse = -inf) carry no weight and their partial rows are never read.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                                                 int H, int S, __bf16* __restrict__ out, float* __restrict__ lse_out) {
+  const int b = blockIdx.y;
+  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (head >= H) return;
+  const float* lp = lse_part + (int64_t)b * S * H + head;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[(int64_t)s * H]);
+  f32x4 acc0 = {}, acc1 = {};
+  float W = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float ls = lp[(int64_t)s * H];
+      if (ls == -INFINITY) continue;
+      const float w = expf(ls - M);
+      W += w;
+      const float* src = o_part + (((int64_t)b * S + s) * H + head) * kDc + 8 * lane;
+      acc0 += w * *(const f32x4*)src;
+      acc1 += w * *(const f32x4*)(src + 4);
+    }
+  }
+  const float inv = (M != -INFINITY) ? 1.0f / W : 0.0f;
+  acc0 *= inv;
+  acc1 *= inv;
+  const u32x4 packed = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                        pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
+  *(u32x4*)(out + ((int64_t)b * H + head) * kDc + 8 * lane) = packed;
+  if (lse_out && lane == 0) lse_out[b * H + head] = (M != -INFINITY) ? M + logf(W) : -INFINITY;
+}
+
+// ---------------------------------------------------------------- launchers
+
+constexpr size_t kDecodeLds = 2 * (size_t)kTile * sizeof(__bf16);  // 74752 bytes
+
+template <int F, bool D>
+static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
+  static bool attr_done = false;  // benign race: the attribute is idempotent
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_decode<F, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kDecodeLds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL((k_decode<F, D>), dim3(a.num_splits, batch), dim3(kThreads), kDecodeLds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream) {
+  if (fmt == kC4R4) return direct ? launch_one<kC4R4, true>(a, batch, stream) : launch_one<kC4R4, false>(a, batch, stream);
+  if (fmt == kC2R4) return direct ? launch_one<kC2R4, true>(a, batch, stream) : launch_one<kC2R4, false>(a, batch, stream);
+  return direct ? launch_one<kBF16, true>(a, batch, stream) : launch_one<kBF16, false>(a, batch, stream);
+}
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, int batch, int heads, int splits,
+                          __bf16* out, float* lse_out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_combine, dim3((heads + 3) / 4, batch), dim3(256), 0, stream, o_part, lse_part, heads, splits,
+                     out, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

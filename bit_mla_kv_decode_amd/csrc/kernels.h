@@ -1,0 +1,30 @@
+// Internal launch interface between the C ABI and the kernels.
+#pragma once
+#include "common.h"
+
+namespace mla {
+
+struct DecodeArgs {
+  const __bf16* q;
+  const uint8_t* cache;
+  int64_t num_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int heads;
+  int max_pages;
+  int num_splits;
+  int pages_per_split;
+  float scale_log2;      // softmax scale * log2(e)
+  float* o_part;         // [B][S][H][512]
+  float* lse_part;       // [B][S][H]
+  __bf16* out;           // [B][H][512] (direct mode)
+  float* lse_out;        // [B][H] or null (direct mode)
+};
+
+hipError_t launch_quant_append(int fmt, const void* latent, const void* rope, const int32_t* slots, int n_new,
+                               void* cache, int64_t num_pages, hipStream_t stream);
+hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_combine(const float* o_part, const float* lse_part, int batch, int heads, int splits,
+                          __bf16* out, float* lse_out, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,169 @@
+/*
+ * mla_lowbit.h -- C ABI of the gfx950 (MI355X) low-bit MLA cache library.
+ *
+ * What the library computes.  In weight-absorbed MLA decode every query head
+ * attends over one shared per-token content latent (d_c = 512) that serves as
+ * both key and value, plus one small decoupled RoPE key (d_r = 64) that
+ * carries position.  QuantMLA keeps both parts of that cache at low bit width
+ * (content INT4 or INT2, RoPE key INT4) and unpacks and dequantizes them inside
+ * the attention kernel.  Sources: "QuantMLA: INT4 (and INT2) for both halves of
+ * the MLA cache" (TL;DR, flowchart, Key findings), "Hugging Face Releases
+ * QuantMLA" (Engineering Trade-offs and Performance), and "QuantMLA's
+ * INT4/INT2 KV-cache quantization reports 5x long-context throughput over
+ * BF16" (What the low-bit cache changes, for the C4R4 name).
+ *
+ * Conventions for every call:
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronizes.  Work is enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL is the null stream) and runs
+ *    asynchronously.
+ *  - bf16 tensors are IEEE bfloat16 bit patterns, row-major, 16-byte aligned.
+ *  - Host-visible arguments are validated before anything is launched; a
+ *    failure returns a non-OK status and mla_last_error() describes it.
+ *    Device-resident values (slot ids, block-table entries, sequence lengths)
+ *    are preconditions: entries outside the page pool are skipped rather than
+ *    dereferenced, but the results for the affected rows are then unspecified.
+ *  - No exception crosses the ABI.  The library is thread-safe for concurrent
+ *    calls on different streams (it keeps no mutable global state apart from
+ *    a thread-local error string).
+ */
+#ifndef MLA_LOWBIT_H
+#define MLA_LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or count  */
+    MLA_ERR_UNSUPPORTED = 2,  /* format or head count this build does not run */
+    MLA_ERR_WORKSPACE = 3,    /* workspace smaller than mla_decode_workspace_bytes */
+    MLA_ERR_HIP = 4           /* the HIP runtime refused a launch            */
+} mla_status_t;
+
+/* Cache encoding.  Supported values:
+ *   C4R4 = {4, 64, 4, 64, 512, 64, 64}: content INT4 in groups of 64 channels,
+ *          RoPE key INT4 in one group of 64;
+ *   C2R4 = {2, 32, 4, 64, 512, 64, 64}: content INT2 in groups of 32 channels,
+ *          RoPE key INT4 in one group of 64;
+ *   BF16 = {16, 0, 16, 0, 512, 64, 64}: unquantized bf16 rows (the baseline).
+ * Quantization is per token and per channel group, asymmetric, with an fp16
+ * scale S and an fp16 zero Z: S = fp16((max - min) / (2^b - 1)), Z = fp16(min),
+ * code = clamp(round_half_even((x - Z) / S), 0, 2^b - 1) in IEEE fp32 with the
+ * stored S and Z (all codes 0 when S == 0), and the dequantized value used by
+ * attention is bf16_round_half_even(fma(code, S, Z)). */
+typedef struct {
+    int32_t c_bits, c_group;   /* content latent: bits (4, 2 or 16), group size */
+    int32_t r_bits, r_group;   /* RoPE key: bits (4 or 16), group size          */
+    int32_t d_c, d_r;          /* 512, 64                                       */
+    int32_t page_size;         /* tokens per page: 64                           */
+} mla_format_t;
+
+/* Physical page layout (bytes, little endian), page = page_size tokens.
+ * Quantized formats:
+ *   [A] content codes   [chunk][token][16 B]: chunk j holds channels
+ *       [j*E, (j+1)*E), E = 128 / c_bits; element e of a chunk is in byte
+ *       e*b/8 at bit (e*b)%8 (INT4: low nibble first; INT2: low pair first);
+ *   [B] content S/Z     [group][token][S16, Z16];
+ *   [C] RoPE codes      [chunk][token][16 B], as [A] with d_r and r_bits;
+ *   [D] RoPE S/Z        [group][token][S16, Z16].
+ * C4R4 page: 16384 + 2048 + 2048 + 256 = 20736 B (324 B per token);
+ * C2R4 page:  8192 + 4096 + 2048 + 256 = 14592 B (228 B per token).
+ * BF16 page: [token][d_c + d_r] bf16 = 73728 B (1152 B per token).
+ * A token's slot is page_id * page_size + offset_in_page. */
+
+/* Bytes per token / per page of `fmt`; 0 if the format is unsupported. */
+size_t mla_token_bytes(const mla_format_t* fmt);
+size_t mla_page_bytes(const mla_format_t* fmt);
+
+/* Quantize and pack n_new new tokens into the paged cache.
+ *   latent_bf16   [n_new, d_c]     content latent rows
+ *   rope_bf16     [n_new, d_r]     RoPE key rows (RoPE already applied)
+ *   slot_mapping  [n_new] int32    destination slot of each row; a negative
+ *                                  slot skips the row; a slot whose page is
+ *                                  >= num_pages is skipped
+ *   cache         [num_pages * mla_page_bytes(fmt)] bytes, written in place
+ * Only the slots named are written (codes, S and Z of every group of the
+ * token).  For BF16 the rows are copied unchanged.  n_new == 0 is a no-op.
+ * Inputs must be finite with each group's (max - min) / (2^b - 1) and min
+ * inside the fp16 range (otherwise S or Z saturate: unspecified codes). */
+mla_status_t mla_quant_append(const mla_format_t* fmt,
+                              const void* latent_bf16, const void* rope_bf16,
+                              const int32_t* slot_mapping, int32_t n_new,
+                              void* cache, int64_t num_pages, void* stream);
+
+/* Split count the library picks for a decode of this shape (num_splits == 0),
+ * from the batch size, the longest sequence and the number of compute units;
+ * always in [1, 64]. */
+int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
+                              int32_t max_seq_len);
+
+/* Workspace bytes mla_decode_lowbit / mla_decode_partial need for this shape:
+ * fp32 partial outputs [batch, num_splits, num_heads, d_c] followed by fp32
+ * partial log-sum-exps [batch, num_splits, num_heads] (256-byte aligned). */
+size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
+                                  int32_t num_splits);
+
+/* Decode attention over the packed cache, for one query token per sequence:
+ *   out[b, h, :] = sum_t softmax_t(scale * <q[b,h,:], khat[t,:]>) * khat[t, :d_c]
+ *   lse[b, h]    = log sum_t exp(scale * <q[b,h,:], khat[t,:]>)   (natural log)
+ * where khat[t] is token t's dequantized [latent | RoPE key] (576 values) and
+ * t runs over the first seq_lens[b] tokens of sequence b, found through
+ * block_table[b, t / page_size] at offset t % page_size.
+ *   q_bf16        [batch, num_heads, d_c + d_r]  absorbed content query then
+ *                                                RoPE query, per head
+ *   cache         as written by mla_quant_append, num_pages pages
+ *   block_table   [batch, max_pages_per_seq] int32 physical page ids
+ *   seq_lens      [batch] int32 tokens per sequence (0 gives out = 0 and
+ *                 lse = -inf; values above max_pages_per_seq * page_size are
+ *                 clamped to that capacity)
+ *   num_heads     1..128
+ *   max_seq_len   host upper bound on seq_lens (used to pick num_splits)
+ *   num_splits    0 = automatic, else 1..64 contiguous page ranges per
+ *                 sequence computed in parallel and merged by log-sum-exp
+ *   workspace     >= mla_decode_workspace_bytes(fmt, batch, num_heads, S)
+ *                 device bytes (S = the split count used); may be NULL when
+ *                 the split count used is 1
+ *   out_bf16      [batch, num_heads, d_c]
+ *   lse_out       [batch, num_heads] fp32, or NULL
+ * Results do not depend on how pages are placed in the pool, and are
+ * bit-identical from run to run for the same split count. */
+mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16,
+                               const void* cache, int64_t num_pages,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
+                               int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes,
+                               void* out_bf16, float* lse_out, void* stream);
+
+/* The two stages of mla_decode_lowbit, for callers that schedule them
+ * separately (for example to merge partial results computed elsewhere).
+ * mla_decode_partial writes, for split s of sequence b, the normalized
+ * partial output over that split's pages and its log-sum-exp (-inf for an
+ * empty split) into `workspace` (layout of mla_decode_workspace_bytes).
+ * mla_decode_combine merges them into out_bf16 / lse_out.  Split s of
+ * sequence b covers pages [s * P, (s + 1) * P) with
+ * P = ceil(ceil(max_seq_len / page_size) / num_splits), the last split running
+ * to the end of the sequence; both stages must be given the same num_splits
+ * (the resolved count when 0 was passed: see mla_decode_num_splits). */
+mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16,
+                                const void* cache, int64_t num_pages,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
+                                int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream);
+mla_status_t mla_decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
+                                int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                                void* out_bf16, float* lse_out, void* stream);
+
+/* Description of the most recent non-OK status returned on this thread. */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_LOWBIT_H */

@@ -1,0 +1,121 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+symbol the header declares, answers the format/size queries, and rejects bad
+host-visible arguments before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_mla_kv_decode_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_lowbit.h")
+
+# fake, 256-byte-aligned device addresses: validation never dereferences them
+A = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x20000)
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_symbols_are_exported():
+    lib = mla.load_library()
+    names = _declared()
+    assert {"mla_quant_append", "mla_decode_lowbit", "mla_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_format_queries():
+    assert mla.mla_page_bytes("C4R4") == 20736 and mla.mla_token_bytes("C4R4") == 324
+    assert mla.mla_page_bytes("C2R4") == 14592 and mla.mla_token_bytes("C2R4") == 228
+    assert mla.mla_page_bytes("BF16") == 73728 and mla.mla_token_bytes("BF16") == 1152
+    for bad in [(4, 32, 4, 64, 512, 64, 64), (8, 64, 4, 64, 512, 64, 64), (4, 64, 4, 64, 512, 64, 32),
+                (4, 64, 2, 64, 512, 64, 64), (4, 64, 4, 64, 256, 64, 64)]:
+        assert mla.mla_page_bytes(bad) == 0 and mla.mla_token_bytes(bad) == 0
+
+
+def test_split_heuristic_and_workspace():
+    f = "C4R4"
+    assert mla.mla_decode_num_splits(f, 1, 16, 256) == 4
+    assert mla.mla_decode_num_splits(f, 32, 128, 8192) == 8
+    assert mla.mla_decode_num_splits(f, 64, 128, 32768) == 4
+    assert mla.mla_decode_num_splits(f, 8, 128, 131072) == 32
+    assert mla.mla_decode_num_splits(f, 128, 128, 131072) == 16
+    assert mla.mla_decode_num_splits(f, 1, 128, 64) == 1
+    assert mla.mla_decode_num_splits(f, 0, 128, 1000) == 1
+    for B, H, S in [(8, 128, 32), (1, 1, 1), (3, 17, 5)]:
+        n = B * S * H
+        expect = (n * 512 * 4 + 255) // 256 * 256 + (n * 4 + 255) // 256 * 256
+        assert mla.mla_decode_workspace_bytes(f, B, H, S) == expect
+    assert mla.mla_decode_workspace_bytes(f, 8, 0, 4) == 0
+
+
+def _fmt(name="C4R4"):
+    return ctypes.byref(mla.format_struct(name))
+
+
+def test_quant_append_argument_errors():
+    L = mla.load_library()
+    assert L.mla_quant_append(_fmt((4, 64, 4, 64, 512, 64, 32)), A, A, A, 4, A, 4, None) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_quant_append(_fmt(), A, A, A, -1, A, 4, None) == mla.MLA_ERR_INVALID_ARG
+    assert "n_new" in mla.mla_last_error()
+    assert L.mla_quant_append(_fmt(), None, A, A, 4, A, 4, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_quant_append(_fmt(), A, A, A, 4, A, 0, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_quant_append(_fmt(), ctypes.c_void_p(0x10008), A, A, 4, A, 4, None) == mla.MLA_ERR_INVALID_ARG
+    assert "aligned" in mla.mla_last_error()
+    # nothing to do: OK without touching a device
+    assert L.mla_quant_append(_fmt(), None, None, None, 0, None, 0, None) == mla.MLA_OK
+
+
+def _decode(fmt="C4R4", q=A, cache=A, num_pages=10, bt=A, sl=A, batch=2, heads=128, max_pages=4, max_len=256,
+            scale=0.07, splits=0, ws=A2, ws_bytes=1 << 30, out=A, lse=None):
+    L = mla.load_library()
+    return L.mla_decode_lowbit(_fmt(fmt), q, cache, num_pages, bt, sl, batch, heads, max_pages, max_len, scale,
+                               splits, ws, ws_bytes, out, lse, None)
+
+
+def test_decode_argument_errors():
+    assert _decode(fmt=(2, 64, 4, 64, 512, 64, 64)) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(heads=0) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(heads=129) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(batch=-1) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(batch=70000) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(max_pages=0) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(num_pages=0) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(splits=65) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(splits=-1) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(scale=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(q=None) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(q=ctypes.c_void_p(0x10002)) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(out=None) == mla.MLA_ERR_INVALID_ARG
+    # 4 splits need a workspace of the documented size
+    need = mla.mla_decode_workspace_bytes("C4R4", 2, 128, 4)
+    assert _decode(splits=4, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert _decode(splits=4, ws=None) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(splits=4, ws=ctypes.c_void_p(0x10010)) == mla.MLA_ERR_INVALID_ARG
+    # empty batch: nothing launched
+    assert _decode(batch=0, q=None, cache=None, bt=None, sl=None, out=None) == mla.MLA_OK
+
+
+def test_combine_argument_errors():
+    L = mla.load_library()
+    need = mla.mla_decode_workspace_bytes("C4R4", 2, 8, 3)
+    assert L.mla_decode_combine(_fmt(), 2, 8, 0, A2, need, A, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_combine(_fmt(), 2, 8, 3, A2, need - 4, A, None, None) == mla.MLA_ERR_WORKSPACE
+    assert L.mla_decode_combine(_fmt(), 2, 0, 3, A2, need, A, None, None) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_decode_combine(_fmt(), 2, 8, 3, A2, need, None, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_combine(_fmt(), 0, 8, 3, None, 0, None, None, None) == mla.MLA_OK
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 512, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        mla.mla_quant_append("C4R4", x, torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(4, dtype=torch.int32),
+                             torch.zeros(20736, dtype=torch.uint8))

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+mla_quant_append must be bit-exact (codes, scales, zeros: whole pages);
+decode outputs must satisfy |out - ref| <= 2e-3 + 1e-2 |ref| elementwise
+against the fp64 oracle run on the same quantized cache.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_mla_kv_decode_amd as mla
+import oracle
+from bit_mla_kv_decode_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-2
+OFMT = {"C4R4": oracle.C4R4, "C2R4": oracle.C2R4, "BF16": oracle.BF16}
+SCALE = float(np.float32(1.0 / math.sqrt(192.0)))
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def build(fmt, lens, heads, seed, outliers=False, pages="random", extra_pages=3):
+    """Host rows + page table for a batch of sequences of the given lengths."""
+    w = W.Workload("case", fmt, batch=len(lens), heads=heads, outliers=outliers, pages=pages, seed=seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    bt, npages = W.page_table(w, lens, extra_pages)
+    lat, rope, slots = [], [], []
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        l, r = W.sequence_rows(w, b, 0, int(L), "cpu")
+        lat.append(l)
+        rope.append(r)
+        slots.append(W.slots_for(bt, b, 0, int(L)))
+    lat = torch.cat(lat) if lat else torch.zeros(0, 512, dtype=torch.bfloat16)
+    rope = torch.cat(rope) if rope else torch.zeros(0, 64, dtype=torch.bfloat16)
+    slots = np.concatenate(slots) if slots else np.zeros(0, np.int32)
+    q = W.queries(w, "cpu")
+    return w, lens, bt, npages, lat, rope, slots, q
+
+
+def gpu_cache(fmt, npages, lat, rope, slots):
+    cache = mla.alloc_cache(fmt, npages)
+    if len(slots):
+        mla.mla_quant_append(fmt, lat.cuda(), rope.cuda(), torch.from_numpy(slots).cuda(), cache)
+    torch.cuda.synchronize()
+    return cache
+
+
+def oracle_cache(fmt, npages, lat, rope, slots):
+    cache = np.zeros(npages * oracle.page_bytes(OFMT[fmt]), dtype=np.uint8)
+    if len(slots):
+        oracle.quant_append(OFMT[fmt], lat, rope, slots, cache, npages)
+    return cache
+
+
+def gpu_decode(fmt, q, cache, bt, lens, splits=0, heads=None):
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device="cuda")
+    out, _ = mla.mla_decode_lowbit(fmt, q.cuda(), cache, torch.from_numpy(bt).cuda(),
+                                   torch.from_numpy(lens).cuda(), SCALE, max_seq_len=int(lens.max()),
+                                   num_splits=splits, lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def assert_close(out, ref, what=""):
+    err = np.abs(out - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    bad = err > bound
+    assert not bad.any(), "%s: %d of %d outside tolerance, worst err %.3g at ref %.3g" % (
+        what, int(bad.sum()), bad.size, float(err.max()), float(ref.flat[int(np.argmax(err - bound))]))
+
+
+def assert_lse(lse, ref):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref))
+    assert np.allclose(lse[fin], ref[fin], rtol=1e-5, atol=1e-4)
+
+
+# ------------------------------------------------------------------ append
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "BF16"])
+def test_quant_append_bit_exact(fmt):
+    _say("append %s" % fmt)
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, [700, 129, 1, 64], 8, seed=11, outliers=True)
+    # special rows: constant groups, signed zeros, exact ties and a skipped slot
+    lat = lat.clone()
+    lat[0] = 0.0
+    lat[1, :64] = -0.0
+    lat[1, 64:] = 1.5
+    lat[2] = torch.arange(512, dtype=torch.float32).remainder(16).to(torch.bfloat16)
+    lat[3, :32] = torch.tensor([0.0, 3.0] + [0.5, 1.5, 2.5] * 10, dtype=torch.float32).to(torch.bfloat16)
+    slots = slots.copy()
+    slots[5] = -1
+    g = gpu_cache(fmt, npages, lat, rope, slots).cpu().numpy()
+    o = oracle_cache(fmt, npages, lat, rope, slots)
+    assert np.array_equal(g, o), "%d bytes differ" % int((g != o).sum())
+
+
+def test_quant_append_skips_out_of_pool_slots():
+    fmt = "C4R4"
+    lat = torch.randn(3, 512).to(torch.bfloat16)
+    rope = torch.randn(3, 64).to(torch.bfloat16)
+    slots = np.array([5, 2 * 64 + 1, 70], dtype=np.int32)     # middle one is past a 2-page pool
+    g = gpu_cache(fmt, 2, lat, rope, slots).cpu().numpy()
+    o = oracle_cache(fmt, 2, lat[[0, 2]], rope[[0, 2]], slots[[0, 2]])
+    assert np.array_equal(g, o)
+
+
+# ------------------------------------------------------------------ decode
+
+CASES = [
+    ("C4R4", [256], 16, 0),                         # tiny decode shape
+    ("C4R4", [1, 31, 32, 33, 64, 65, 200, 1000], 128, 0),
+    ("C4R4", [1, 31, 32, 33, 64, 65, 200, 1000], 128, 1),
+    ("C4R4", [1000, 130, 7], 128, 5),
+    ("C2R4", [1, 33, 95, 640, 999], 128, 0),
+    ("C2R4", [500, 64], 33, 3),
+    ("BF16", [1, 33, 95, 640], 128, 0),
+    ("BF16", [300], 48, 2),
+    ("C4R4", [77, 512], 1, 0),
+    ("C2R4", [2048], 64, 0),
+]
+
+
+@pytest.mark.parametrize("fmt,lens,heads,splits", CASES)
+def test_decode_matches_oracle(fmt, lens, heads, splits):
+    _say("decode %s lens=%s H=%d S=%d" % (fmt, lens, heads, splits))
+    outl = fmt == "C2R4"
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, lens, heads, seed=len(lens) + heads, outliers=outl)
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    host = cache.cpu().numpy()
+    assert np.array_equal(host, oracle_cache(fmt, npages, lat, rope, slots))
+    out, lse = gpu_decode(fmt, q, cache, bt, lens, splits)
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, host, npages, bt, lens, SCALE)
+    assert_close(out, ref, "%s %s" % (fmt, list(lens)))
+    assert_lse(lse, ref_lse)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_empty_sequences(splits):
+    fmt = "C4R4"
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, [0, 100, 0, 64], 128, seed=3)
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    out, lse = gpu_decode(fmt, q, cache, bt, lens, splits)
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, cache.cpu().numpy(), npages, bt, lens, SCALE)
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    assert np.isneginf(lse[0]).all() and np.isneginf(lse[2]).all()
+    assert_close(out, ref)
+    assert_lse(lse, ref_lse)
+
+
+def test_large_logit_jump_recomputes_split():
+    """Logits that rise by far more than 2^64 after the first tile (the kernel's
+    fixed-reference range) must still give the exact softmax."""
+    fmt = "C4R4"
+    L = 300
+    g = torch.Generator().manual_seed(5)
+    lat = (torch.randn(L, 512, generator=g) * 0.05)
+    lat[100:110, 0] = 60.0 + torch.arange(10, dtype=torch.float32)   # huge keys late in the sequence
+    lat[250, 7] = -40.0
+    lat = lat.to(torch.bfloat16)
+    rope = torch.randn(L, 64, generator=g).to(torch.bfloat16)
+    q = torch.randn(1, 128, 576, generator=g)
+    q[0, :, 0] = 40.0 * torch.rand(128, generator=g)
+    q = q.to(torch.bfloat16)
+    bt = np.arange(5, dtype=np.int32)[None]
+    lens = np.array([L], np.int32)
+    slots = np.arange(L, dtype=np.int32)
+    cache = gpu_cache(fmt, 5, lat, rope, slots)
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, cache.cpu().numpy(), 5, bt, lens, SCALE)
+    for splits in (1, 2):
+        out, lse = gpu_decode(fmt, q, cache, bt, lens, splits)
+        assert_close(out, ref, "splits=%d" % splits)
+        assert_lse(lse, ref_lse)
+
+
+def test_invariances_bitwise():
+    """Same split count -> bit-identical across runs and page placements; other
+    split counts agree with the oracle."""
+    fmt = "C2R4"
+    lens = [900, 333, 64]
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, lens, 128, seed=9, outliers=True)
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    a1, l1 = gpu_decode(fmt, q, cache, bt, lens, 3)
+    a2, l2 = gpu_decode(fmt, q, cache, bt, lens, 3)
+    assert np.array_equal(a1, a2) and np.array_equal(l1, l2)
+    # place the same tokens into a different page permutation (appended one token per call)
+    w2 = W.derive(w, pages="random", seed=w.seed + 100)
+    bt2, np2 = W.page_table(w2, lens, 7)
+    slots2 = np.concatenate([W.slots_for(bt2, b, 0, int(L)) for b, L in enumerate(lens)])
+    cache2 = mla.alloc_cache(fmt, np2)
+    lat_d, rope_d, s_d = lat.cuda(), rope.cuda(), torch.from_numpy(slots2).cuda()
+    for i0 in range(0, len(slots2), 97):
+        mla.mla_quant_append(fmt, lat_d[i0:i0 + 97], rope_d[i0:i0 + 97], s_d[i0:i0 + 97], cache2)
+    b1, m1 = gpu_decode(fmt, q, cache2, bt2, lens, 3)
+    assert np.array_equal(a1, b1) and np.array_equal(l1, m1)
+    ref, _ = oracle.decode(OFMT[fmt], q, cache.cpu().numpy(), npages, bt, lens, SCALE)
+    for s in (1, 2, 7, 64):
+        o, _ = gpu_decode(fmt, q, cache, bt, lens, s)
+        assert_close(o, ref, "splits=%d" % s)
+
+
+def test_partial_then_combine_equals_fused():
+    fmt = "C4R4"
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, [700, 90], 128, seed=21)
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    S = 4
+    ws = torch.empty(mla.mla_decode_workspace_bytes(fmt, 2, 128, S), dtype=torch.uint8, device="cuda")
+    qd, btd, sld = q.cuda(), torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+    mla.mla_decode_partial(fmt, qd, cache, btd, sld, SCALE, S, ws, max_seq_len=700)
+    out = torch.empty(2, 128, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(2, 128, dtype=torch.float32, device="cuda")
+    mla.mla_decode_combine(fmt, 2, 128, S, ws, out, lse)
+    o_part, l_part = mla.workspace_views(fmt, ws, 2, 128, S)
+    # every partial matches the oracle on its own token range
+    host = cache.cpu().numpy()
+    pps = -(-((700 + 63) // 64) // S)
+    for s in range(S):
+        t0, t1 = s * pps * 64, ((s + 1) * pps * 64 if s < S - 1 else 10**9)
+        ro, rl = oracle.decode(OFMT[fmt], q, host, npages, bt, lens, SCALE, t_begin=t0, t_end=t1)
+        got = o_part[:, s].cpu().numpy()
+        gl = l_part[:, s].cpu().numpy()
+        for b in range(2):
+            if np.isneginf(rl[b]).all():
+                assert np.isneginf(gl[b]).all()
+                continue
+            assert np.allclose(got[b], ro[b], rtol=1e-4, atol=1e-4)
+            assert np.allclose(gl[b], rl[b], rtol=1e-5, atol=1e-4)
+    fused, flse = gpu_decode(fmt, q, cache, bt, lens, S)
+    assert np.array_equal(out.float().cpu().numpy(), fused)
+    assert np.array_equal(lse.cpu().numpy(), flse)
