@@ -1,0 +1,197 @@
+"""Benchmark: low-bit MLA decode serving step on one MI355X.
+
+One step = the whole hot path over one batch:
+  1. mla_quant_append: quantize + pack the new token of every sequence
+     (position L_b - 1) into the paged cache;
+  2. mla_decode_partial: split-KV attention over the packed cache;
+  3. mla_decode_combine: log-sum-exp merge of the splits.
+The default workload is the long-context C4R4 decode: 8 sequences x 131072
+tokens, 128 heads (d_c = 512 latent + d_r = 64 RoPE key), 64-token pages.
+Inputs are synthetic and resident in HBM before timing; the cache is
+replicated so consecutive steps read different copies (no reuse through the
+256 MB last-level cache).
+
+Prints ONE JSON line on stdout.  `value` = packed cache bytes read by the
+decode per step / step time (GB/s).  `roofline` describes the split-KV decode
+kernel (its average duration from HIP events on its stream), `cpu_baseline`
+the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn cache GB/s + % HBM peak (C4R4/C2R4, 128 heads, 32K–128K ctx)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_workload(w, device, replicas):
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    from bit_mla_kv_decode_amd import workloads as W
+    lens = W.seq_lens(w)
+    bt, npages = W.page_table(w, lens)
+    caches = [mla.alloc_cache(w.fmt, npages, device) for _ in range(replicas)]
+    for b, L in enumerate(lens):
+        # rows are generated on the GPU in 32K-token pieces and packed by the library
+        for t0 in range(0, int(L), 32768):
+            t1 = min(int(L), t0 + 32768)
+            lat, rope = W.sequence_rows(w, b, t0, t1, device)
+            slots = torch.from_numpy(W.slots_for(bt, b, t0, t1)).to(device)
+            for c in caches:
+                mla.mla_quant_append(w.fmt, lat, rope, slots, c)
+    torch.cuda.synchronize()
+    q = W.queries(w, device)
+    new_lat, new_rope = W.new_token_rows(w, lens, device)
+    new_slots = torch.from_numpy(np.array([W.slots_for(bt, b, int(L) - 1, int(L))[0]
+                                           for b, L in enumerate(lens)], dtype=np.int32)).to(device)
+    return lens, bt, npages, caches, q, new_lat, new_rope, new_slots
+
+
+def cpu_baseline(w, seqs=2):
+    """Oracle decode (fp64) on the first `seqs` sequences, all heads, on the host cores."""
+    import oracle
+    from bit_mla_kv_decode_amd import workloads as W
+    lens = W.seq_lens(w)[:seqs]
+    wq = W.derive(w, batch=len(lens))
+    bt, npages = W.page_table(W.derive(w, pages="contiguous"), lens)
+    fmt = {"C4R4": oracle.C4R4, "C2R4": oracle.C2R4, "BF16": oracle.BF16}[w.fmt]
+    cache = np.zeros(npages * oracle.page_bytes(fmt), dtype=np.uint8)
+    for b, L in enumerate(lens):
+        lat, rope = W.sequence_rows(w, b, 0, int(L), "cpu")
+        oracle.quant_append(fmt, lat, rope, W.slots_for(bt, b, 0, int(L)), cache, npages)
+    q = W.queries(wq, "cpu")
+    threads = min(16, os.cpu_count() or 1)
+    t = time.perf_counter()
+    oracle.decode(fmt, q, cache, npages, bt, lens, w.softmax_scale, nthreads=threads)
+    dt = time.perf_counter() - t
+    tokens = int(lens.sum())
+    from bit_mla_kv_decode_amd import mla_token_bytes
+    gbs = tokens * mla_token_bytes(w.fmt) / dt / 1e9
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences (%d tokens), all %d heads, decode only (fp64), %.1f s"
+                      % (len(lens), w.batch, tokens, w.heads, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4r4_128k")
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode shards by sequence; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    from bit_mla_kv_decode_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    mla.load_library()
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    tok_bytes = mla.mla_token_bytes(w.fmt)
+    lens_all = W.seq_lens(w)
+    cache_bytes = int(((lens_all.astype(np.int64) + 63) // 64).sum()) * mla.mla_page_bytes(w.fmt)
+    replicas = max(1, min(4, math.ceil(1.0e9 / cache_bytes)))
+    log("building %s: B=%d H=%d fmt=%s, %.1f MB packed cache x %d replicas"
+        % (w.name, w.batch, w.heads, w.fmt, cache_bytes / 1e6, replicas))
+    lens, bt, npages, caches, q, new_lat, new_rope, new_slots = build_workload(w, dev, replicas)
+    B, H = w.batch, w.heads
+    max_len = int(lens.max())
+    S = args.splits or mla.mla_decode_num_splits(w.fmt, B, H, max_len)
+    ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, H, S), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    bt_d = torch.from_numpy(bt).to(dev)
+    sl_d = torch.from_numpy(lens).to(dev)
+    stream = torch.cuda.current_stream()
+    tokens = int(lens.sum())
+    packed_bytes = tokens * tok_bytes
+    flops = tokens * 2.0 * H * (576 + 512)          # algorithmic: Q.K^T over 576 + P.V over 512
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i, timed=None):
+        c = caches[i % replicas]
+        mla.mla_quant_append(w.fmt, new_lat, new_rope, new_slots, c, stream=stream)
+        if timed is not None:
+            timed[0].record(stream)
+        mla.mla_decode_partial(w.fmt, q, c, bt_d, sl_d, w.softmax_scale, S, ws, max_seq_len=max_len,
+                               stream=stream)
+        if timed is not None:
+            timed[1].record(stream)
+        mla.mla_decode_combine(w.fmt, B, H, S, ws, out, lse, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ms_step = total * 1e3 / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = packed_bytes / (ms_step * 1e-3) / 1e9
+    k_tflops = flops / (k_ms * 1e-3) / 1e12
+    log("step %.3f ms, decode kernel %.3f ms: %.1f GB/s packed (%.1f%% of HBM), %.1f TFLOP/s (%.1f%% of bf16 MFMA)"
+        % (ms_step, k_ms, value, 100 * value / HBM_PEAK_GBS, k_tflops, 100 * k_tflops / BF16_MFMA_PEAK_TFLOPS))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(w)
+        log("cpu baseline: %s" % cpu)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "format": w.fmt, "batch": B, "heads": H, "ctx": max_len,
+                   "tokens": tokens, "splits": S, "page_size": 64, "cache_replicas": replicas,
+                   "step": "quant_append(1 token/seq) + split-KV decode + LSE combine",
+                   "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "k_decode (split-KV partial)", "bound": "mfma",
+                     "achieved": round(k_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(k_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(k_ms, 4), "flops_per_launch": flops,
+                     "packed_bytes_per_launch": packed_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,15 +40,28 @@ namespace mla {
 
 constexpr int kTileTok = 32;                // tokens per tile (half a page)
 constexpr int kRow = kD + 8;                // LDS row stride in bf16: 1168 B
-constexpr int kTile = kTileTok * kRow;      // elements per tile buffer (40 KB)
+constexpr int kTile = kTileTok * kRow;      // elements per tile buffer (37376 bytes)
+// q channels [0, kQLds) of all heads are staged in LDS (rows padded to 528
+// bytes so 16 heads reading the same chunk hit distinct banks); the remaining
+// channels stay in registers.  This keeps the hot loop free of spills.
+constexpr int kQLds = 256;
+constexpr int kQRow = kQLds + 8;
+constexpr int kQRegSteps = (kD - kQLds) / 16;   // 20 k-steps of 16 channels in registers
 constexpr int kThreads = 256;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// LDS tile: row r (token) at r * 1168 bytes, 16-byte chunk c (channels
-// 8c .. 8c + 7) at byte 16 c.  1168 = 144 (mod 256), so 16 consecutive rows
-// reading the same chunk hit distinct banks.  Addresses stay affine in the
-// loop indices, so they fold into instruction offsets.
+// LDS tile: 32 rows of 1168 bytes (576 bf16 + 16 bytes of padding); token t
+// of the tile lives in row rho(t), which transposes every 4 x 4 block of
+// tokens inside a group of 16: rho(16u + 4q + j) = 16u + 4j + q.  Chunk c
+// (channels 8c .. 8c + 7) of a row is at byte 16 c.  With 1168 = 144 (mod 256):
+//  - 16 consecutive rows read at the same chunk (Q.K^T operand reads, one
+//    16-lane pass of ds_read_b128) fall in 16 distinct 16-byte bank groups;
+//  - the 4 tokens a transposing read gathers (4q' + j, j < 4) sit in rows
+//    4 apart, i.e. in 4 distinct 64-byte bank blocks, so the 32 lanes of a
+//    pass (4 rows x 64 bytes) are conflict-free as well.
+// All addresses stay affine in the unrolled loop indices.
+__device__ __forceinline__ int rho(int t) { return (t & ~15) + 4 * (t & 3) + ((t >> 2) & 3); }
 __device__ __forceinline__ int tile_off(int r, int chunk) { return r * kRow + 8 * chunk; }
 
 __device__ __forceinline__ float wave_partner(float v) {
@@ -61,10 +74,19 @@ __device__ __forceinline__ float wave_partner(float v) {
 
 // ---------------------------------------------------------------- dequantization
 
+// w & m, opaque to the optimizer: keeps the byte-wise conversions below as
+// v_cvt_f32_ubyte{0..3} on the masked word instead of one bitfield extract
+// per element.
+__device__ __forceinline__ unsigned mask_bytes(unsigned w, unsigned m) {
+  unsigned r;
+  asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
+  return r;
+}
+
 // 8 INT4 codes of one dword (element e at bits 4e) -> 8 bf16 values.
 __device__ __forceinline__ bf16x8 dq_int4(unsigned w, float S, float Z) {
-  const unsigned lo = w & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
-  const unsigned hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  const unsigned lo = mask_bytes(w, 0x0F0F0F0Fu);        // elements 0, 2, 4, 6
+  const unsigned hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);   // elements 1, 3, 5, 7
   u32x4 r;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -78,8 +100,8 @@ __device__ __forceinline__ bf16x8 dq_int4(unsigned w, float S, float Z) {
 // 16 INT2 codes of one dword (element e at bits 2e), all of one group -> 16 bf16 values.
 __device__ __forceinline__ void dq_int2(unsigned w, float S, float Z, bf16x8& o0, bf16x8& o1) {
   // byte k of (w >> 2j) & 0x03030303 holds element 4k + j
-  const unsigned b0 = w & 0x03030303u, b1 = (w >> 2) & 0x03030303u;
-  const unsigned b2 = (w >> 4) & 0x03030303u, b3 = (w >> 6) & 0x03030303u;
+  const unsigned b0 = mask_bytes(w, 0x03030303u), b1 = mask_bytes(w >> 2, 0x03030303u);
+  const unsigned b2 = mask_bytes(w >> 4, 0x03030303u), b3 = mask_bytes(w >> 6, 0x03030303u);
   u32x4 r0, r1;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -109,13 +131,22 @@ __device__ __forceinline__ void sz_unpack(unsigned sz, float& S, float& Z) {
 
 template <int F> struct Fill;
 
+// Every thread also dequantizes 8 RoPE channels of its token: channels
+// [8 cs, 8 cs + 8), i.e. dword cs % 4 of RoPE chunk cs / 4.
+// The dequantization of a tile is split into kSubsteps small steps (one packed
+// pair of bf16 values each, a 16-byte LDS write every 4 steps) so the kernel
+// can place one step after each P.V MFMA of the previous tile.
+
 template <> struct Fill<kC4R4> {
   using Lay = PageLayout<kC4R4>;
+  static constexpr int kSubsteps = 36;  // 9 dwords (8 content + 1 RoPE) x 4 pairs
   u32x4 c[2];
   unsigned sz[2];
-  u32x4 r;
-  unsigned rsz;
+  unsigned r, rsz;
   bool ok;
+  // working state of the dword being converted
+  unsigned lo, hi, outw[4];
+  float S, Z;
   __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
     const int t = (threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
     ok = page >= 0 && page < num_pages;
@@ -126,40 +157,44 @@ template <> struct Fill<kC4R4> {
       c[i] = *(const u32x4*)(base + Lay::kCodesA + (j * kPage + t) * 16);
       sz[i] = *(const unsigned*)(base + Lay::kSzB + ((j >> 1) * kPage + t) * 4);
     }
-    if (cs < 2) {
-      r = *(const u32x4*)(base + Lay::kCodesC + (cs * kPage + t) * 16);
-      rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+    r = *(const unsigned*)(base + Lay::kCodesC + ((cs >> 2) * kPage + t) * 16 + 4 * (cs & 3));
+    rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+  }
+  // step u: dword p = u / 4 (p < 8: content chunk cs + 8 (p / 4), dword p % 4;
+  // p = 8: RoPE), pair q = u % 4 (elements 2q, 2q + 1 of the dword)
+  __device__ __forceinline__ void substep(__bf16* tile, int nvalid, int u) {
+    const int t = threadIdx.x & 31, cs = threadIdx.x >> 5;
+    const int p = u >> 2, q = u & 3;
+    if (q == 0) {
+      const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
+      const unsigned w = p < 8 ? c[p >> 2][p & 3] : r;
+      sz_unpack(live ? (p < 8 ? sz[p >> 2] : rsz) : 0u, S, Z);
+      lo = mask_bytes(w, 0x0F0F0F0Fu);        // elements 0, 2, 4, 6
+      hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);   // elements 1, 3, 5, 7
+    }
+    const float a = __builtin_fmaf((float)((lo >> (8 * q)) & 0xFFu), S, Z);
+    const float b = __builtin_fmaf((float)((hi >> (8 * q)) & 0xFFu), S, Z);
+    outw[q] = pack_bf16x2(a, b);
+    if (q == 3) {
+      const int chunk = p < 8 ? 4 * (cs + 8 * (p >> 2)) + (p & 3) : 64 + cs;
+      *(u32x4*)(tile + rho(t) * kRow + 8 * chunk) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
     }
   }
-  __device__ __forceinline__ void store(__bf16* tile, int nvalid) const {
-    const int t = threadIdx.x & 31, cs = threadIdx.x >> 5;
-    const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
+  __device__ __forceinline__ void store(__bf16* tile, int nvalid) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = cs + 8 * i;
-      float S, Z;
-      sz_unpack(live ? sz[i] : 0u, S, Z);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *(bf16x8*)(tile + tile_off(t, 4 * j + v)) = dq_int4(live ? c[i][v] : 0u, S, Z);
-    }
-    if (cs < 2) {
-      float S, Z;
-      sz_unpack(live ? rsz : 0u, S, Z);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *(bf16x8*)(tile + tile_off(t, 64 + 4 * cs + v)) = dq_int4(live ? r[v] : 0u, S, Z);
-    }
+    for (int u = 0; u < kSubsteps; ++u) substep(tile, nvalid, u);
   }
 };
 
 template <> struct Fill<kC2R4> {
   using Lay = PageLayout<kC2R4>;
+  static constexpr int kSubsteps = 36;  // 4 content dwords x 8 pairs + 1 RoPE dword x 4 pairs
   u32x4 c;
   unsigned sz[2];
-  u32x4 r;
-  unsigned rsz;
+  unsigned r, rsz;
   bool ok;
+  unsigned b0, b1, b2, b3, outw[4];
+  float S, Z;
   __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
     const int t = (threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
     ok = page >= 0 && page < num_pages;
@@ -168,31 +203,50 @@ template <> struct Fill<kC2R4> {
     c = *(const u32x4*)(base + Lay::kCodesA + (cs * kPage + t) * 16);
     sz[0] = *(const unsigned*)(base + Lay::kSzB + ((2 * cs) * kPage + t) * 4);
     sz[1] = *(const unsigned*)(base + Lay::kSzB + ((2 * cs + 1) * kPage + t) * 4);
-    if (cs < 2) {
-      r = *(const u32x4*)(base + Lay::kCodesC + (cs * kPage + t) * 16);
-      rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
-    }
+    r = *(const unsigned*)(base + Lay::kCodesC + ((cs >> 2) * kPage + t) * 16 + 4 * (cs & 3));
+    rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
   }
-  __device__ __forceinline__ void store(__bf16* tile, int nvalid) const {
+  // steps 0..31: content dword v = u / 8 (channels [64 cs + 16 v, +16), group
+  // 2 cs + v / 2), pair q = u % 8 (elements 2q, 2q + 1); steps 32..35: RoPE
+  __device__ __forceinline__ void substep(__bf16* tile, int nvalid, int u) {
     const int t = threadIdx.x & 31, cs = threadIdx.x >> 5;
     const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      // dword v = channels [64 cs + 16 v, +16), group 2 cs + v / 2
-      float S, Z;
-      sz_unpack(live ? sz[v >> 1] : 0u, S, Z);
-      bf16x8 x0, x1;
-      dq_int2(live ? c[v] : 0u, S, Z, x0, x1);
-      *(bf16x8*)(tile + tile_off(t, 8 * cs + 2 * v)) = x0;
-      *(bf16x8*)(tile + tile_off(t, 8 * cs + 2 * v + 1)) = x1;
+    __bf16* row = tile + rho(t) * kRow;
+    if (u < 32) {
+      const int v = u >> 3, q = u & 7;
+      if (q == 0) {
+        sz_unpack(live ? sz[v >> 1] : 0u, S, Z);
+        const unsigned w = c[v];
+        // byte k of (w >> 2j) & 0x03030303 holds element 4k + j
+        b0 = mask_bytes(w, 0x03030303u);
+        b1 = mask_bytes(w >> 2, 0x03030303u);
+        b2 = mask_bytes(w >> 4, 0x03030303u);
+        b3 = mask_bytes(w >> 6, 0x03030303u);
+      }
+      // elements 2q, 2q + 1 = byte k = q / 2, bit pairs (2q % 4), (2q % 4) + 1
+      const int k = q >> 1;
+      const unsigned ba = (q & 1) ? b2 : b0, bb = (q & 1) ? b3 : b1;
+      const float ea = __builtin_fmaf((float)((ba >> (8 * k)) & 0xFFu), S, Z);
+      const float eb = __builtin_fmaf((float)((bb >> (8 * k)) & 0xFFu), S, Z);
+      outw[q & 3] = pack_bf16x2(ea, eb);
+      if ((q & 3) == 3)
+        *(u32x4*)(row + 8 * (8 * cs + 2 * v + (q >> 2))) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
+    } else {
+      const int q = u - 32;
+      if (q == 0) {
+        sz_unpack(live ? rsz : 0u, S, Z);
+        b0 = mask_bytes(r, 0x0F0F0F0Fu);
+        b1 = mask_bytes(r >> 4, 0x0F0F0F0Fu);
+      }
+      const float ea = __builtin_fmaf((float)((b0 >> (8 * q)) & 0xFFu), S, Z);
+      const float eb = __builtin_fmaf((float)((b1 >> (8 * q)) & 0xFFu), S, Z);
+      outw[q] = pack_bf16x2(ea, eb);
+      if (q == 3) *(u32x4*)(row + 8 * (64 + cs)) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
     }
-    if (cs < 2) {
-      float S, Z;
-      sz_unpack(live ? rsz : 0u, S, Z);
+  }
+  __device__ __forceinline__ void store(__bf16* tile, int nvalid) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *(bf16x8*)(tile + tile_off(t, 64 + 4 * cs + v)) = dq_int4(live ? r[v] : 0u, S, Z);
-    }
+    for (int u = 0; u < kSubsteps; ++u) substep(tile, nvalid, u);
   }
 };
 
@@ -201,8 +255,10 @@ template <> struct Fill<kC2R4> {
 // the page past the sequence end are read (they are inside the page) and
 // replaced by zeros.
 template <> struct Fill<kBF16> {
+  static constexpr int kSubsteps = 0;
   const uint8_t* base;
   bool ok;
+  __device__ __forceinline__ void substep(__bf16*, int, int) {}
   __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
     ok = page >= 0 && page < num_pages;
     base = cache + (ok ? page : 0) * (int64_t)PageLayout<kBF16>::kBytes + hp * (kTileTok * kD * 2);
@@ -219,13 +275,36 @@ template <> struct Fill<kBF16> {
         const int t = ci / 72, col = ci % 72;
         const bool live = ok && t < nvalid;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *(u32x4*)(tile + tile_off(t, col)) = live ? v[i] : z;
+        *(u32x4*)(tile + tile_off(rho(t), col)) = live ? v[i] : z;
       }
     }
   }
 };
 
 // ---------------------------------------------------------------- decode kernel
+
+// Block-table window for the tiles [k0, k1) of a split: lane i holds the id of
+// page wbase + i, so the page of a tile comes from v_readlane without a
+// memory wait; the window moves every 64 pages.
+struct PageWindow {
+  const int32_t* bt;
+  int p_end, wbase, ids;
+  __device__ __forceinline__ PageWindow(const int32_t* bt_, int k0, int k1) : bt(bt_) {
+    p_end = (k1 + 1) >> 1;
+    wbase = k0 >> 1;
+    const int lane = threadIdx.x & 63;
+    ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
+  }
+  __device__ __forceinline__ int page_of(int kt) {
+    const int pg = kt >> 1;
+    if (pg - wbase >= 64) {  // uniform; once per 64 pages
+      wbase = pg;
+      const int lane = threadIdx.x & 63;
+      ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
+    }
+    return __builtin_amdgcn_readlane(ids, pg - wbase);
+  }
+};
 
 // Result of one pass over a split, per lane: O^T accumulators (channels x the
 // lane's head), softmax denominator part and reference.
@@ -246,13 +325,16 @@ constexpr float kMaxLift = 64.0f;
 
 template <int F>
 __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int k0,
-                                           int k1, const bf16x8 (&qr)[36], bool fixed, float m_fixed,
+                                           int k1, const bf16x8 (&qr)[kQRegSteps], bool fixed, float m_fixed,
                                            SplitAcc& acc) {
   const int lane = threadIdx.x & 63, hi = lane >> 5;
+  const __bf16* qrow = smem + 2 * kTile + ((threadIdx.x >> 6) * 32 + (lane & 31)) * kQRow + 8 * hi;
   // transposing-read addresses for the P.V operand: lane (g, i) = (lane / 16,
   // lane % 16) reads 4 channels of one token row; see the kernel comment.
   const int g = lane >> 4, i16 = lane & 15;
-  const int tr_row0 = 4 * (g >> 1) + (i16 >> 2);        // token quad 0 or 1 of a 16-token step
+  // token 4 quad + i16 / 4 of a 16-token step sits in row 4 (i16 / 4) + quad;
+  // quad = g / 2 for the first 4 k-slots of the lane, 2 + g / 2 for the next 4
+  const int tr_row0 = 4 * (i16 >> 2) + (g >> 1);
   const int tr_chunk = 2 * (g & 1) + ((i16 & 3) >> 1);   // + 4 ct
   const int tr_half = 4 * (i16 & 1);
 
@@ -263,68 +345,109 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
   acc.m_seen = -INFINITY;
   bool lifted = false;
 
+  PageWindow win(bt, k0, k1);
+
   Fill<F> fill;
-  fill.load(a.cache, bt[k0 >> 1], k0 & 1, a.num_pages);
+  fill.load(a.cache, win.page_of(k0), k0 & 1, a.num_pages);
   fill.store(smem, min(kTileTok, L - k0 * kTileTok));
   __syncthreads();
 
   for (int k = k0; k < k1; ++k) {
     __bf16* tile = smem + ((k - k0) & 1) * kTile;
     __bf16* next = smem + ((k - k0 + 1) & 1) * kTile;
-    const bool more = k + 1 < k1;
-    if (more) fill.load(a.cache, bt[(k + 1) >> 1], (k + 1) & 1, a.num_pages);
+    // next tile's loads (the last iteration reloads its own tile: harmless,
+    // keeps the loop body a single basic block so VALU and MFMA interleave)
+    const int kn = min(k + 1, k1 - 1);
+    fill.load(a.cache, win.page_of(kn), kn & 1, a.num_pages);
 
     const int nvalid = min(kTileTok, L - k * kTileTok);
-    // ---- S^T = khat . q^T for the 32 tokens of the tile
+    // ---- S^T = khat . q^T for the 32 tokens of the tile.  Operands are read
+    //      4 k-steps ahead; scheduling barriers pin that order so LDS latency
+    //      hides behind the MFMAs instead of stalling each one.
     f32x16 s = {};
-    const int arow = lane & 31;
+    const __bf16* arow = tile + rho(lane & 31) * kRow + 8 * hi;
+    bf16x8 kv[4], qv[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      kv[d] = *(const bf16x8*)(arow + 16 * d);
+      qv[d] = *(const bf16x8*)(qrow + 16 * d);
+    }
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
-      const bf16x8 kv = *(const bf16x8*)(tile + tile_off(arow, 2 * ks + hi));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qr[ks], s, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 bq = ks < 16 ? qv[ks & 3] : qr[ks < 16 ? 0 : ks - 16];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks & 3], bq, s, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 4 < 36) kv[ks & 3] = *(const bf16x8*)(arow + 16 * (ks + 4));
+      if (ks + 4 < 16) qv[ks & 3] = *(const bf16x8*)(qrow + 16 * (ks + 4));
     }
+    __builtin_amdgcn_sched_barrier(0);
     // ---- softmax weights (log2 domain); reg r is token 8 (r / 4) + 4 hi + r % 4
-    float x[16];
-    float mt = -INFINITY;
+    if (nvalid < kTileTok) {  // only the sequence's last tile is partial
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t0 = 8 * (r >> 2) + 4 * hi + (r & 3);
-      x[r] = t0 < nvalid ? s[r] * a.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, x[r]);
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[r] = -INFINITY;
     }
-    mt = fmaxf(mt, wave_partner(mt));
+    float smax = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
+    const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
     acc.m_seen = fmaxf(acc.m_seen, mt);
     if (k == k0 && !fixed) acc.m_ref = mt;
-    lifted |= mt - acc.m_ref > kMaxLift;
+    lifted |= mt - acc.m_ref > kMaxLift;   // p may overflow below: the pass is then redone
+    const float neg_ref = -acc.m_ref;
     float ps = 0.0f;
     unsigned phi[8], plo[8];  // packed bf16 pairs: P high part and remainder
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float pa = exp2f(fminf(x[r] - acc.m_ref, kMaxLift));
-      const float pb = exp2f(fminf(x[r + 1] - acc.m_ref, kMaxLift));
+      // v_exp_f32 directly: weights below 2^-126 of the reference flush to 0
+      const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, neg_ref));
+      const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.scale_log2, neg_ref));
       ps += pa + pb;
       const unsigned h2 = pack_bf16x2(pa, pb);
       phi[r >> 1] = h2;
       plo[r >> 1] = pack_bf16x2(pa - bf16_lo(h2), pb - bf16_hi(h2));
     }
     acc.l_sum += ps;
-    // ---- O^T += khat^T . P  (k-step kk covers tile tokens 16 kk .. 16 kk + 15)
+    // ---- O^T += khat^T . P  (k-step kk covers tile tokens 16 kk .. 16 kk + 15);
+    //      the next tile's dequantization pieces are spread between the MFMAs
+    const int nvalid_next = min(kTileTok, L - (k + 1) * kTileTok);
+    constexpr int kSub = Fill<F>::kSubsteps;
+    bf16x8 bp[2][2];  // [kk][hi/lo]
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 bh = __builtin_bit_cast(bf16x8, (u32x4){phi[4 * kk], phi[4 * kk + 1], phi[4 * kk + 2], phi[4 * kk + 3]});
-      const bf16x8 bl = __builtin_bit_cast(bf16x8, (u32x4){plo[4 * kk], plo[4 * kk + 1], plo[4 * kk + 2], plo[4 * kk + 3]});
-      const __bf16* v0 = tile + (16 * kk + tr_row0) * kRow + 8 * tr_chunk + tr_half;
-      const __bf16* v1 = v0 + 8 * kRow;
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + 32 * ct));
-        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v1 + 32 * ct));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bh, acc.o[ct], 0, 0, 0);
-        acc.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bl, acc.o[ct], 0, 0, 0);
-      }
+      bp[kk][0] = __builtin_bit_cast(bf16x8, (u32x4){phi[4 * kk], phi[4 * kk + 1], phi[4 * kk + 2], phi[4 * kk + 3]});
+      bp[kk][1] = __builtin_bit_cast(bf16x8, (u32x4){plo[4 * kk], plo[4 * kk + 1], plo[4 * kk + 2], plo[4 * kk + 3]});
     }
-    if (more) fill.store(next, min(kTileTok, L - (k + 1) * kTileTok));
+    // step = 16 kk + ct: A operand = khat^T for channels [32 ct, 32 ct + 32) and
+    // the 16 tokens of k-step kk, read 3 steps ahead.  Scheduling fences pin
+    // the order MFMA / dequantization step / MFMA / ..., so that the VALU work
+    // for the next tile issues in the shadow of the matrix pipe.
+    const __bf16* vbase = tile + tr_row0 * kRow + 8 * tr_chunk + tr_half;
+    auto tr_read = [&](int step) {
+      const __bf16* v0 = vbase + 16 * (step >> 4) * kRow + 32 * (step & 15);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v0);
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + 2 * kRow));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 va[3];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) va[d] = tr_read(d);
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      const int kk = step >> 4, ct = step & 15;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % 3], bp[kk][h], acc.o[ct], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = 2 * step + h - (64 - kSub);   // dequantization steps in the last kSub slots
+        if (u >= 0 && u < kSub) fill.substep(next, nvalid_next, u);
+      }
+      if (step + 3 < 32) va[step % 3] = tr_read(step + 3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kSub == 0) fill.store(next, nvalid_next);
     __syncthreads();
   }
   return lifted;
@@ -335,14 +458,15 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
 template <int F>
 __device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L,
                                                      int k0, int k1) {
+  PageWindow win(bt, k0, k1);
   Fill<F> fill;
-  fill.load(a.cache, bt[k0 >> 1], k0 & 1, a.num_pages);
+  fill.load(a.cache, win.page_of(k0), k0 & 1, a.num_pages);
   fill.store(smem, min(kTileTok, L - k0 * kTileTok));
   __syncthreads();
   for (int k = k0; k < k1; ++k) {
     __bf16* next = smem + ((k - k0 + 1) & 1) * kTile;
     if (k + 1 < k1) {
-      fill.load(a.cache, bt[(k + 1) >> 1], (k + 1) & 1, a.num_pages);
+      fill.load(a.cache, win.page_of(k + 1), (k + 1) & 1, a.num_pages);
       fill.store(next, min(kTileTok, L - (k + 1) * kTileTok));
     }
     __syncthreads();
@@ -410,6 +534,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
   const int k1 = min(2 * p1, (L + kTileTok - 1) / kTileTok);
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
+  // stage q[b, :, 0:256] (zeros for heads >= H); the first tile's barrier publishes it
+  {
+    __bf16* ql = smem + 2 * kTile;
+    for (int ci = tid; ci < 128 * (kQLds / 8); ci += kThreads) {
+      const int h = ci / (kQLds / 8), c = ci % (kQLds / 8);
+      bf16x8 v = {};
+      if (h < H) v = *(const bf16x8*)(a.q + ((int64_t)b * H + h) * kD + 8 * c);
+      *(bf16x8*)(ql + h * kQRow + 8 * c) = v;
+    }
+  }
+
   if (wave * 32 >= H) {  // no heads for this wavefront: fill only (uniform per wave)
     for (int pass = 0;; ++pass) {
       split_pass_fill_only<F>(a, smem, bt, L, k0, k1);
@@ -420,14 +555,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
 
   const int head = wave * 32 + (lane & 31);
   const int hi = lane >> 5;
-  // q^T operand: lane holds head `head`, channels 16 ks + 8 hi + [0, 8)
-  bf16x8 qr[36];
+  // q^T operand: lane holds head `head`; channels [256, 576) in registers
+  // (16 ks + 8 hi + [0, 8), ks >= 16), channels [0, 256) of every head in LDS
+  bf16x8 qr[kQRegSteps];
   {
     const int hq = head < H ? head : H - 1;
-    const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi;
+    const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + kQLds + 8 * hi;
     const bf16x8 zero = {};
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
+    for (int ks = 0; ks < kQRegSteps; ++ks) {
       const bf16x8 v = *(const bf16x8*)(qh + 16 * ks);
       qr[ks] = head < H ? v : zero;
     }
@@ -486,7 +622,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_par
 
 // ---------------------------------------------------------------- launchers
 
-constexpr size_t kDecodeLds = 2 * (size_t)kTile * sizeof(__bf16);  // 74752 bytes
+constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
 
 template <int F, bool D>
 static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
