@@ -62,7 +62,7 @@ def build_workload(w, device, replicas):
     return lens, bt, npages, caches, q, new_lat, new_rope, new_slots
 
 
-def cpu_baseline(w, seqs=2):
+def cpu_baseline(w, seqs=8):
     """Oracle decode (fp64) on the first `seqs` sequences, all heads, on the host cores."""
     import oracle
     from bit_mla_kv_decode_amd import workloads as W
@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4r4_128k")
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--heads", type=int, default=0, help="override the workload's head count (head sweep)")
+    ap.add_argument("--format", default="", help="override the cache format: C4R4, C2R4 or BF16 (same data)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -111,6 +113,10 @@ def main():
     mla.load_library()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
+    if args.heads:
+        w = W.derive(w, heads=args.heads)
+    if args.format:
+        w = W.derive(w, fmt=args.format)
     tok_bytes = mla.mla_token_bytes(w.fmt)
     lens_all = W.seq_lens(w)
     cache_bytes = int(((lens_all.astype(np.int64) + 63) // 64).sum()) * mla.mla_page_bytes(w.fmt)
@@ -160,6 +166,18 @@ def main():
     log("step %.3f ms, decode kernel %.3f ms: %.1f GB/s packed (%.1f%% of HBM), %.1f TFLOP/s (%.1f%% of bf16 MFMA)"
         % (ms_step, k_ms, value, 100 * value / HBM_PEAK_GBS, k_tflops, 100 * k_tflops / BF16_MFMA_PEAK_TFLOPS))
 
+    # the decode kernel's binding roof: MFMA when its algorithmic intensity is
+    # above the MI355X ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), else HBM
+    intensity = flops / packed_bytes
+    if intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        bound, achieved, peak, unit = "mfma", k_tflops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", packed_bytes / (k_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    roofline = {"kernel": "k_decode (split-KV partial)", "bound": bound, "achieved": round(achieved, 2),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel_ms": round(k_ms, 4), "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
+                "intensity_flop_per_byte": round(intensity, 1)}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
@@ -183,11 +201,7 @@ def main():
                    "tokens": tokens, "splits": S, "page_size": 64, "cache_replicas": replicas,
                    "step": "quant_append(1 token/seq) + split-KV decode + LSE combine",
                    "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "k_decode (split-KV partial)", "bound": "mfma",
-                     "achieved": round(k_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel_ms": round(k_ms, 4), "flops_per_launch": flops,
-                     "packed_bytes_per_launch": packed_bytes},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -41,12 +41,17 @@ namespace mla {
 constexpr int kTileTok = 32;                // tokens per tile (half a page)
 constexpr int kRow = kD + 8;                // LDS row stride in bf16: 1168 B
 constexpr int kTile = kTileTok * kRow;      // elements per tile buffer (37376 bytes)
-// q channels [0, kQLds) of all heads are staged in LDS (rows padded to 528
-// bytes so 16 heads reading the same chunk hit distinct banks); the remaining
-// channels stay in registers.  This keeps the hot loop free of spills.
+// q of all heads is split between LDS and registers by k-step (16 channels):
+// the even k-steps 0, 2, .., 30 (256 channels) are staged in LDS (rows padded
+// to 528 bytes so 16 heads reading the same chunk hit distinct banks), the
+// odd k-steps 1, .., 31 and 32..35 stay in registers.  Interleaving keeps the
+// Q.K^T loop at no more than two LDS operand reads per MFMA pair, and the
+// register share keeps the hot loop free of spills.
 constexpr int kQLds = 256;
 constexpr int kQRow = kQLds + 8;
 constexpr int kQRegSteps = (kD - kQLds) / 16;   // 20 k-steps of 16 channels in registers
+__device__ __forceinline__ constexpr bool q_in_lds(int ks) { return ks < 32 && (ks & 1) == 0; }
+__device__ __forceinline__ constexpr int q_reg_index(int ks) { return ks < 32 ? ks >> 1 : ks - 16; }
 constexpr int kThreads = 256;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -315,13 +320,17 @@ struct SplitAcc {
   float m_seen;  // true max logit of the head over the split (log2 units)
 };
 
-// Softmax weights are taken against a fixed reference per split: the first
-// tile's max (pass 1), so O never needs rescaling and stays in MFMA
-// accumulators.  Later tiles may exceed it; p = 2^(x - m_ref) is allowed up to
-// 2^kMaxLift, which keeps l and O far inside the fp32 range.  If any logit of
-// the split lies more than kMaxLift above the reference, the pass reports it
-// and the caller recomputes the split with m_ref = the split's true max.
-constexpr float kMaxLift = 64.0f;
+// Softmax weights are taken against a fixed reference per split, so O never
+// needs rescaling and stays in MFMA accumulators.  The reference is the first
+// tile's max plus kRefLift (log2 units): weights of tokens more than
+// 126 - kRefLift below that max flush to zero (they are below 2^-86 of the
+// largest weight), and later tiles may rise up to kRefLift + kMaxLift above
+// it with p <= 2^kMaxLift, which keeps l and O below 2^113 even for 2^17
+// tokens of magnitude 2^16.  If any logit of the split lies more than
+// kMaxLift above the reference, the pass reports it and the caller recomputes
+// the split with the reference set to the split's true max.
+constexpr float kRefLift = 40.0f;
+constexpr float kMaxLift = 80.0f;
 
 template <int F>
 __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int k0,
@@ -366,20 +375,19 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
     //      hides behind the MFMAs instead of stalling each one.
     f32x16 s = {};
     const __bf16* arow = tile + rho(lane & 31) * kRow + 8 * hi;
-    bf16x8 kv[4], qv[4];
+    bf16x8 kv[4], qv[2];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      kv[d] = *(const bf16x8*)(arow + 16 * d);
-      qv[d] = *(const bf16x8*)(qrow + 16 * d);
-    }
+    for (int d = 0; d < 4; ++d) kv[d] = *(const bf16x8*)(arow + 16 * d);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) qv[d] = *(const bf16x8*)(qrow + 16 * d);   // k-steps 0, 2
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 bq = ks < 16 ? qv[ks & 3] : qr[ks < 16 ? 0 : ks - 16];
+      const bf16x8 bq = q_in_lds(ks) ? qv[(ks >> 1) & 1] : qr[q_in_lds(ks) ? 0 : q_reg_index(ks)];
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks & 3], bq, s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (ks + 4 < 36) kv[ks & 3] = *(const bf16x8*)(arow + 16 * (ks + 4));
-      if (ks + 4 < 16) qv[ks & 3] = *(const bf16x8*)(qrow + 16 * (ks + 4));
+      if (q_in_lds(ks) && ks + 4 < 32) qv[(ks >> 1) & 1] = *(const bf16x8*)(qrow + 16 * ((ks >> 1) + 2));
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- softmax weights (log2 domain); reg r is token 8 (r / 4) + 4 hi + r % 4
@@ -388,13 +396,13 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[r] = -INFINITY;
     }
-    float smax = s[0];
+    if (k == k0 && !fixed) {  // a pass's reference: the first tile's max (uniform branch)
+      float smax = s[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
-    const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
-    acc.m_seen = fmaxf(acc.m_seen, mt);
-    if (k == k0 && !fixed) acc.m_ref = mt;
-    lifted |= mt - acc.m_ref > kMaxLift;   // p may overflow below: the pass is then redone
+      for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
+      acc.m_ref = fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift;
+    }
+    // the weights need only the fixed reference, not this tile's max
     const float neg_ref = -acc.m_ref;
     float ps = 0.0f;
     unsigned phi[8], plo[8];  // packed bf16 pairs: P high part and remainder
@@ -407,6 +415,17 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
       const unsigned h2 = pack_bf16x2(pa, pb);
       phi[r >> 1] = h2;
       plo[r >> 1] = pack_bf16x2(pa - bf16_lo(h2), pb - bf16_hi(h2));
+    }
+    // this tile's max (log2 units): tracks the split's true max and detects a
+    // rise beyond 2^kMaxLift above the reference (the weights above may then
+    // have overflowed: the pass is redone with the true max)
+    {
+      float smax = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
+      const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
+      acc.m_seen = fmaxf(acc.m_seen, mt);
+      lifted |= mt - acc.m_ref > kMaxLift;
     }
     acc.l_sum += ps;
     // ---- O^T += khat^T . P  (k-step kk covers tile tokens 16 kk .. 16 kk + 15);
@@ -534,13 +553,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
   const int k1 = min(2 * p1, (L + kTileTok - 1) / kTileTok);
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  // stage q[b, :, 0:256] (zeros for heads >= H); the first tile's barrier publishes it
+  // stage the LDS k-steps of q (zeros for heads >= H): LDS chunk c of head h
+  // holds channels 16 (2 (c / 2)) + 8 (c % 2) + [0, 8); the first tile's
+  // barrier publishes it
   {
     __bf16* ql = smem + 2 * kTile;
     for (int ci = tid; ci < 128 * (kQLds / 8); ci += kThreads) {
       const int h = ci / (kQLds / 8), c = ci % (kQLds / 8);
       bf16x8 v = {};
-      if (h < H) v = *(const bf16x8*)(a.q + ((int64_t)b * H + h) * kD + 8 * c);
+      if (h < H) v = *(const bf16x8*)(a.q + ((int64_t)b * H + h) * kD + 32 * (c >> 1) + 8 * (c & 1));
       *(bf16x8*)(ql + h * kQRow + 8 * c) = v;
     }
   }
@@ -555,21 +576,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
 
   const int head = wave * 32 + (lane & 31);
   const int hi = lane >> 5;
-  // q^T operand: lane holds head `head`; channels [256, 576) in registers
-  // (16 ks + 8 hi + [0, 8), ks >= 16), channels [0, 256) of every head in LDS
+  // q^T operand: lane holds head `head`, channels 16 ks + 8 hi + [0, 8) of the
+  // register k-steps (odd ks < 32, and 32..35); the even ks < 32 are in LDS
   bf16x8 qr[kQRegSteps];
   {
     const int hq = head < H ? head : H - 1;
-    const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + kQLds + 8 * hi;
+    const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi;
     const bf16x8 zero = {};
 #pragma unroll
-    for (int ks = 0; ks < kQRegSteps; ++ks) {
+    for (int ks = 0; ks < 36; ++ks) {
+      if (q_in_lds(ks)) continue;
       const bf16x8 v = *(const bf16x8*)(qh + 16 * ks);
-      qr[ks] = head < H ? v : zero;
+      qr[q_reg_index(ks)] = head < H ? v : zero;
     }
   }
-  // pass 0 takes the first tile's max as reference; a second pass (rare) uses
-  // the split's true max found by pass 0.
+  // pass 0 takes the first tile's max (plus kRefLift) as reference; a second
+  // pass (only when a logit rises more than kRefLift + kMaxLift above that
+  // max) uses the split's true max found by pass 0.
   bool fixed = false;
   float m_fixed = 0.0f;
   for (int pass = 0;; ++pass) {

@@ -156,9 +156,12 @@ def test_empty_sequences(splits):
     assert_lse(lse, ref_lse)
 
 
-def test_large_logit_jump_recomputes_split():
-    """Logits that rise by far more than 2^64 after the first tile (the kernel's
-    fixed-reference range) must still give the exact softmax."""
+@pytest.mark.parametrize("qmax", [40.0, 11.0])
+def test_large_logit_jump(qmax):
+    """Logits that rise far above the first tile's after it: with qmax = 40 the
+    rise (up to ~250 in log2 units) exceeds the kernel's fixed-reference range
+    and the split is recomputed; with qmax = 11 (rises up to ~70-110) it stays
+    inside the range.  Both must give the exact softmax."""
     fmt = "C4R4"
     L = 300
     g = torch.Generator().manual_seed(5)
@@ -168,7 +171,7 @@ def test_large_logit_jump_recomputes_split():
     lat = lat.to(torch.bfloat16)
     rope = torch.randn(L, 64, generator=g).to(torch.bfloat16)
     q = torch.randn(1, 128, 576, generator=g)
-    q[0, :, 0] = 40.0 * torch.rand(128, generator=g)
+    q[0, :, 0] = qmax * torch.rand(128, generator=g)
     q = q.to(torch.bfloat16)
     bt = np.arange(5, dtype=np.int32)[None]
     lens = np.array([L], np.int32)
