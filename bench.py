@@ -3,8 +3,9 @@
 One step = the whole hot path over one batch:
   1. mla_quant_append: quantize + pack the new token of every sequence
      (position L_b - 1) into the paged cache;
-  2. mla_decode_partial: split-KV attention over the packed cache;
-  3. mla_decode_combine: log-sum-exp merge of the splits.
+  2. mla_decode_partial: split-KV attention over the packed cache, the
+     batch's pages cut into one equal share per compute unit (num_splits = 0);
+  3. mla_decode_combine: log-sum-exp merge of the pieces.
 The default workload is the long-context C4R4 decode: 8 sequences x 131072
 tokens, 128 heads (d_c = 512 latent + d_r = 64 RoPE key), 64-token pages.
 Inputs are synthetic and resident in HBM before timing; the cache is
@@ -93,7 +94,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4r4_128k")
-    ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="0 = balanced partition over the batch; 1..64 = fixed splits per sequence")
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count (head sweep)")
     ap.add_argument("--format", default="", help="override the cache format: C4R4, C2R4 or BF16 (same data)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -126,7 +128,7 @@ def main():
     lens, bt, npages, caches, q, new_lat, new_rope, new_slots = build_workload(w, dev, replicas)
     B, H = w.batch, w.heads
     max_len = int(lens.max())
-    S = args.splits or mla.mla_decode_num_splits(w.fmt, B, H, max_len)
+    S = args.splits
     ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, H, S), dtype=torch.uint8, device=dev)
     out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, H, dtype=torch.float32, device=dev)
@@ -198,7 +200,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "format": w.fmt, "batch": B, "heads": H, "ctx": max_len,
-                   "tokens": tokens, "splits": S, "page_size": 64, "cache_replicas": replicas,
+                   "tokens": tokens, "page_size": 64, "cache_replicas": replicas,
+                   "partition": "balanced (256 equal page shares)" if S == 0 else "%d splits per sequence" % S,
                    "step": "quant_append(1 token/seq) + split-KV decode + LSE combine",
                    "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,

@@ -169,17 +169,18 @@ def mla_decode_lowbit(fmt, q, cache, block_table, seq_lens, softmax_scale, max_s
                       out=None, lse=None, workspace=None, num_pages=None, stream=None):
     """Decode attention over the packed cache; returns (out bf16 [B, H, 512], lse fp32 [B, H] or None).
 
-    `max_seq_len` is the host-side bound on seq_lens used to choose splits (default: capacity)."""
+    num_splits = 0 balances the batch's pages over all compute units; 1..64
+    splits every sequence into that many page ranges (1: no workspace).
+    `max_seq_len` is the host-side bound on seq_lens (default: capacity)."""
     import torch
     B, H, MP, NP = _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
     if max_seq_len is None:
         max_seq_len = MP * 64
-    S = num_splits or mla_decode_num_splits(fmt, B, H, max_seq_len)
+    S = int(num_splits)
     if out is None:
         out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
-    ws_bytes = mla_decode_workspace_bytes(fmt, B, H, S) if S > 1 else 0
-    if workspace is None and S > 1:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is None and S != 1:
+        workspace = torch.empty(mla_decode_workspace_bytes(fmt, B, H, S), dtype=torch.uint8, device=q.device)
     _check(load_library().mla_decode_lowbit(
         ctypes.byref(format_struct(fmt)), _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.uint8), NP,
         _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
@@ -211,10 +212,28 @@ def mla_decode_combine(fmt, batch, num_heads, num_splits, workspace, out, lse=No
 
 
 def workspace_views(fmt, workspace, batch, num_heads, num_splits):
-    """fp32 views (o_part [B, S, H, 512], lse_part [B, S, H]) of a decode workspace."""
+    """fp32 views (o_part [B, S, H, 512], lse_part [B, S, H]) of a workspace
+    written with num_splits = S >= 1 per-sequence splits."""
     import torch
+    if num_splits < 1:
+        raise ValueError("workspace_views needs the per-sequence split layout (num_splits >= 1)")
     n_o = batch * num_splits * num_heads * 512
     o_bytes = (n_o * 4 + 255) // 256 * 256
     o = workspace[:n_o * 4].view(torch.float32).view(batch, num_splits, num_heads, 512)
     l = workspace[o_bytes:o_bytes + batch * num_splits * num_heads * 4].view(torch.float32)
     return o, l.view(batch, num_splits, num_heads)
+
+
+def balanced_workspace_views(fmt, workspace, batch, num_heads):
+    """Views of a workspace written with num_splits = 0: fp32 o_part
+    [256 + B, H, 512], fp32 lse_part [256 + B, H] (slot w + b holds workgroup
+    w's piece of sequence b) and int32 meta [B, 2] (first slot, slot count)."""
+    import torch
+    slots = 256 + batch
+    n_o = slots * num_heads * 512
+    o_bytes = (n_o * 4 + 255) // 256 * 256
+    l_bytes = (slots * num_heads * 4 + 255) // 256 * 256
+    o = workspace[:n_o * 4].view(torch.float32).view(slots, num_heads, 512)
+    l = workspace[o_bytes:o_bytes + slots * num_heads * 4].view(torch.float32).view(slots, num_heads)
+    m = workspace[o_bytes + l_bytes:o_bytes + l_bytes + batch * 8].view(torch.int32).view(batch, 2)
+    return o, l, m

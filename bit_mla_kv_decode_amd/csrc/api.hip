@@ -26,6 +26,9 @@ mla_status_t fail(mla_status_t s, const char* fmt, ...) {
 constexpr int kComputeUnits = 256;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxPagesPerSplit = 128;
+// 2^24 pages = 2^30 tokens per sequence keeps every in-kernel token and
+// per-64-sequence page count inside int32
+constexpr int kMaxPagesPerSeq = 1 << 24;
 
 int format_id(const mla_format_t* f) {
   if (!f) return -1;
@@ -49,12 +52,26 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Partial-row slots: batch * splits per-sequence splits, or, for the balanced
+// partition (splits == 0), one per (workgroup, sequence) piece: at most
+// kFlatGroups + batch - 1.
+constexpr int kFlatGroups = kComputeUnits;
+size_t slot_count(int batch, int splits) {
+  return splits > 0 ? (size_t)batch * splits : (size_t)kFlatGroups + batch;
+}
+
 size_t partial_o_bytes(int batch, int heads, int splits) {
-  return align_up((size_t)batch * splits * heads * mla::kDc * sizeof(float), 256);
+  return align_up(slot_count(batch, splits) * heads * mla::kDc * sizeof(float), 256);
+}
+
+size_t partial_lse_bytes(int batch, int heads, int splits) {
+  return align_up(slot_count(batch, splits) * heads * sizeof(float), 256);
 }
 
 size_t workspace_bytes(int batch, int heads, int splits) {
-  return partial_o_bytes(batch, heads, splits) + align_up((size_t)batch * splits * heads * sizeof(float), 256);
+  size_t n = partial_o_bytes(batch, heads, splits) + partial_lse_bytes(batch, heads, splits);
+  if (splits == 0) n += align_up((size_t)batch * 2 * sizeof(int), 256);  // per-sequence (first slot, count)
+  return n;
 }
 
 int auto_splits(int batch, int max_seq_len) {
@@ -85,6 +102,9 @@ mla_status_t check_decode(const mla_format_t* fmt, const void* q, const void* ca
   if (num_heads < 1 || num_heads > 128)
     return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128 (got %d)", num_heads);
   if (max_pages_per_seq < 1) return fail(MLA_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
+  if (max_pages_per_seq > kMaxPagesPerSeq)
+    return fail(MLA_ERR_UNSUPPORTED, "max_pages_per_seq above %d is not supported (got %d)", kMaxPagesPerSeq,
+                max_pages_per_seq);
   if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
   if (max_seq_len < 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be >= 0");
   if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
@@ -99,9 +119,9 @@ mla_status_t check_decode(const mla_format_t* fmt, const void* q, const void* ca
   }
   int64_t cap = (int64_t)max_pages_per_seq * mla::kPage;
   int64_t hint = max_seq_len < cap ? max_seq_len : cap;
-  shape->splits = num_splits > 0 ? num_splits : auto_splits(batch, (int)hint);
+  shape->splits = num_splits;  // 0: balanced partition over the whole batch
   const int pages = (int)((hint + mla::kPage - 1) / mla::kPage);
-  int pps = (pages + shape->splits - 1) / shape->splits;
+  int pps = num_splits > 0 ? (pages + num_splits - 1) / num_splits : 1;
   shape->pages_per_split = pps < 1 ? 1 : pps;
   return MLA_OK;
 }
@@ -115,6 +135,7 @@ mla::DecodeArgs make_args(const void* q, const void* cache, int64_t num_pages, c
   a.num_pages = num_pages;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
+  a.batch = batch;
   a.heads = num_heads;
   a.max_pages = max_pages_per_seq;
   a.num_splits = sh.splits;
@@ -123,6 +144,8 @@ mla::DecodeArgs make_args(const void* q, const void* cache, int64_t num_pages, c
   if (workspace) {
     a.o_part = (float*)workspace;
     a.lse_part = (float*)((char*)workspace + partial_o_bytes(batch, num_heads, sh.splits));
+    a.meta = (int*)((char*)workspace + partial_o_bytes(batch, num_heads, sh.splits) +
+                    partial_lse_bytes(batch, num_heads, sh.splits));
   }
   return a;
 }
@@ -162,7 +185,7 @@ int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t nu
 }
 
 size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits) {
-  if (format_id(fmt) < 0 || batch < 0 || num_heads < 1 || num_splits < 1) return 0;
+  if (format_id(fmt) < 0 || batch < 0 || num_heads < 1 || num_splits < 0 || num_splits > kMaxSplits) return 0;
   return workspace_bytes(batch, num_heads, num_splits);
 }
 
@@ -183,7 +206,8 @@ mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16, con
                 workspace_bytes(batch, num_heads, sh.splits));
   mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
                                 max_pages_per_seq, softmax_scale, sh, workspace);
-  hipError_t e = mla::launch_decode(sh.fmt, false, a, batch, (hipStream_t)stream);
+  hipError_t e = sh.splits > 0 ? mla::launch_decode(sh.fmt, false, a, batch, (hipStream_t)stream)
+                               : mla::launch_decode_flat(sh.fmt, a, kFlatGroups, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return MLA_OK;
 }
@@ -194,7 +218,7 @@ mla_status_t mla_decode_combine(const mla_format_t* fmt, int32_t batch, int32_t 
   if (format_id(fmt) < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
   if (batch < 0 || batch > 65535) return fail(MLA_ERR_INVALID_ARG, "batch must be in 0..65535");
   if (num_heads < 1 || num_heads > 128) return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128");
-  if (num_splits < 1 || num_splits > kMaxSplits) return fail(MLA_ERR_INVALID_ARG, "num_splits must be in 1..64");
+  if (num_splits < 0 || num_splits > kMaxSplits) return fail(MLA_ERR_INVALID_ARG, "num_splits must be in 0..64");
   if (batch == 0) return MLA_OK;
   if (!workspace || !out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
   if (!aligned(workspace, 256) || !aligned(out_bf16, 16) || (lse_out && !aligned(lse_out, 4)))
@@ -204,8 +228,12 @@ mla_status_t mla_decode_combine(const mla_format_t* fmt, int32_t batch, int32_t 
                 workspace_bytes(batch, num_heads, num_splits));
   const float* o_part = (const float*)workspace;
   const float* lse_part = (const float*)((const char*)workspace + partial_o_bytes(batch, num_heads, num_splits));
-  hipError_t e = mla::launch_combine(o_part, lse_part, batch, num_heads, num_splits, (__bf16*)out_bf16, lse_out,
-                                     (hipStream_t)stream);
+  const int* meta = (const int*)((const char*)lse_part + partial_lse_bytes(batch, num_heads, num_splits));
+  hipError_t e = num_splits > 0
+                     ? mla::launch_combine(o_part, lse_part, batch, num_heads, num_splits, (__bf16*)out_bf16, lse_out,
+                                           (hipStream_t)stream)
+                     : mla::launch_combine_flat(o_part, lse_part, meta, batch, num_heads, (__bf16*)out_bf16, lse_out,
+                                                (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
   return MLA_OK;
 }

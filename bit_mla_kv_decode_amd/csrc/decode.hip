@@ -492,8 +492,10 @@ __device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16
   }
 }
 
+// Writes one pass result: the final bf16 output (direct mode) or an fp32
+// partial row at a.o_part[row * 512] / a.lse_part[row] (row = slot * H + head).
 template <bool kDirect>
-__device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int split, int head, const SplitAcc& acc) {
+__device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t slot, int head, const SplitAcc& acc) {
   const int hi = (threadIdx.x & 63) >> 5;
   const float l_tot = acc.l_sum + wave_partner(acc.l_sum);
   const float inv = 1.0f / l_tot;
@@ -512,7 +514,7 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int spli
       }
     if (a.lse_out && hi == 0) a.lse_out[b * H + head] = lse;
   } else {
-    const int64_t row = ((int64_t)b * a.num_splits + split) * H + head;
+    const int64_t row = slot * H + head;
     float* orow = a.o_part + row * kDc + 4 * hi;
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct)
@@ -526,33 +528,16 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int spli
   }
 }
 
+// Attention of sequence b over its tiles [k0, k1) (non-empty), written to
+// `slot`.  Called by every thread of the workgroup (uniform control flow).
 template <int F, bool kDirect>
-__global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
-  const int split = blockIdx.x, b = blockIdx.y;
+__device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem, int b, int L, int k0, int k1,
+                                              int64_t slot) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int H = a.heads;
-
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
-  const int n_pages = (L + kPage - 1) / kPage;
-  const int p0 = split * a.pages_per_split;
-  const int p1 = (split == a.num_splits - 1) ? n_pages : min(p0 + a.pages_per_split, n_pages);
-
-  if (p0 >= p1) {  // empty split
-    if (kDirect) {
-      for (int i = tid; i < H * kDc; i += kThreads) a.out[(int64_t)b * H * kDc + i] = (__bf16)0.0f;
-      if (a.lse_out && tid < H) a.lse_out[b * H + tid] = -INFINITY;
-    } else if (tid < H) {
-      a.lse_part[((int64_t)b * a.num_splits + split) * H + tid] = -INFINITY;
-    }
-    return;
-  }
-  // tiles are half pages: tile k covers tokens [32 k, 32 k + 32)
-  const int k0 = 2 * p0;
-  const int k1 = min(2 * p1, (L + kTileTok - 1) / kTileTok);
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
+  __syncthreads();  // the previous range (if any) has finished with LDS
   // stage the LDS k-steps of q (zeros for heads >= H): LDS chunk c of head h
   // holds channels 16 (2 (c / 2)) + 8 (c % 2) + [0, 8); the first tile's
   // barrier publishes it
@@ -600,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
     const bool lifted = split_pass<F>(a, smem, bt, L, k0, k1, qr, fixed, m_fixed, acc);
     const bool redo = __syncthreads_or(lifted);
     if (!redo || pass > 0) {
-      write_split<kDirect>(a, b, split, head, acc);
+      write_split<kDirect>(a, b, slot, head, acc);
       return;
     }
     fixed = true;
@@ -608,30 +593,210 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- combine kernel
+__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
+  const int L = a.seq_lens[b];
+  return L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
+}
+
+// Per-sequence splits: workgroup (split, b) covers pages [split * P, (split + 1) * P)
+// of sequence b, the last split running to the end of the sequence.
+template <int F, bool kDirect>
+__global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int H = a.heads;
+  const int L = clamped_len(a, b);
+  const int n_pages = (L + kPage - 1) / kPage;
+  const int p0 = split * a.pages_per_split;
+  const int p1 = (split == a.num_splits - 1) ? n_pages : min(p0 + a.pages_per_split, n_pages);
+  if (p0 >= p1) {  // empty split
+    if (kDirect) {
+      for (int i = tid; i < H * kDc; i += kThreads) a.out[(int64_t)b * H * kDc + i] = (__bf16)0.0f;
+      if (a.lse_out && tid < H) a.lse_out[b * H + tid] = -INFINITY;
+    } else if (tid < H) {
+      a.lse_part[((int64_t)b * a.num_splits + split) * H + tid] = -INFINITY;
+    }
+    return;
+  }
+  // tiles are half pages: tile k covers tokens [32 k, 32 k + 32)
+  process_range<F, kDirect>(a, smem, b, L, 2 * p0, min(2 * p1, (L + kTileTok - 1) / kTileTok),
+                            (int64_t)b * a.num_splits + split);
+}
+
+// Balanced partition: the batch's pages, laid end to end in sequence order
+// (T pages), are cut into G = min(gridDim.x, T) equal shares, so that no
+// share is empty; workgroup w < G takes pages [w T / G, (w + 1) T / G), which
+// may span the end of one sequence and the start of others.  Each
+// (workgroup, sequence) piece is written to partial slot w + b: the slots of
+// one sequence are consecutive, and the workgroup holding a sequence's first
+// page records (first slot, count) in a.meta[b].
+__device__ __forceinline__ int64_t share_start(int64_t w, int64_t T, int64_t G) { return (w * T) / G; }
+
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+__device__ __forceinline__ unsigned long long uniform64(unsigned long long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Walk of the batch for one workgroup's share, kept in LDS: wavefront 0
+// advances it between barriers, so no walk state stays in registers while
+// the tiles run.  Sequences are taken 64 at a time (a "chunk"): their lengths,
+// first-page offsets and which of them overlap the share.
+struct FlatWalk {
+  long long start, end;  // the share: pages [start, end)
+  long long next;        // pages before the chunk after the current one
+  unsigned long long mask;  // chunk sequences overlapping the share
+  int b0, j;             // current chunk's first sequence; next index to look at
+  int len[64];
+  long long off[64];
+  int piece[4];          // sequence (-1: share done), length, first tile, end tile
+};
+
+// Wavefront 0 only (all 64 lanes): find the next piece of the share and
+// publish it in walk.piece.  A sequence whose first page lies in the share
+// gets its (first slot, slot count) recorded in meta.
+__device__ __forceinline__ void flat_next_piece(const DecodeArgs& a, FlatWalk& walk, int64_t w, int64_t T,
+                                                int64_t G) {
+  const int ln = opaque_lane();
+  const int64_t start = (int64_t)uniform64((unsigned long long)walk.start);
+  const int64_t end = (int64_t)uniform64((unsigned long long)walk.end);
+  int b0 = __builtin_amdgcn_readfirstlane(walk.b0), j = __builtin_amdgcn_readfirstlane(walk.j);
+  unsigned long long mask = uniform64(walk.mask);
+  int pb = -1, pl = 0, pk0 = 0, pk1 = 0;
+  for (;;) {
+    const unsigned long long m = j < 64 ? mask & (~0ull << j) : 0ull;
+    if (m) {
+      const int jj = __builtin_ctzll(m);
+      const int L = __builtin_amdgcn_readfirstlane(walk.len[jj]);
+      const int64_t off = (int64_t)uniform64((unsigned long long)walk.off[jj]);
+      const int64_t n = (L + kPage - 1) / kPage;
+      const int p0 = (int)((off > start ? off : start) - off);
+      const int p1 = (int)((off + n < end ? off + n : end) - off);
+      pb = b0 + jj;
+      pl = L;
+      pk0 = 2 * p0;
+      pk1 = min(2 * p1, (L + kTileTok - 1) / kTileTok);
+      j = jj + 1;
+      break;
+    }
+    const int64_t base = (int64_t)uniform64((unsigned long long)walk.next);
+    if (b0 + 64 >= a.batch || base >= end) break;  // the share is done
+    b0 += 64;
+    j = 0;
+    // scan the chunk's page counts (inclusive prefix sum over the wavefront)
+    const int b = b0 + ln;
+    const int L = b < a.batch ? clamped_len(a, b) : 0;
+    const int n = (L + kPage - 1) / kPage;
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (ln >= d) incl += v;
+    }
+    const int64_t off = base + incl - n;
+    const int64_t lo = off > start ? off : start;
+    const int64_t hi = off + n < end ? off + n : end;
+    const bool seg = b < a.batch && lo < hi;
+    if (seg && off >= start) {
+      // the first page of b is in this share: b's slots run from w + b to
+      // wl + b, wl the share holding b's last page
+      const int64_t x = off + n - 1;
+      int64_t wl = (x * G) / T;
+      while (wl + 1 < G && share_start(wl + 1, T, G) <= x) ++wl;
+      while (share_start(wl, T, G) > x) --wl;
+      a.meta[2 * b] = (int)(w + b);
+      a.meta[2 * b + 1] = (int)(wl - w + 1);
+    }
+    walk.len[ln] = L;
+    walk.off[ln] = off;
+    if (ln == 63) walk.next = base + incl;
+    mask = __ballot(seg);
+  }
+  if (ln == 0) {
+    walk.piece[0] = pb;
+    walk.piece[1] = pl;
+    walk.piece[2] = pk0;
+    walk.piece[3] = pk1;
+    walk.b0 = b0;
+    walk.j = j;
+    walk.mask = mask;
+  }
+}
+
+template <int F>
+__global__ __launch_bounds__(kThreads, 1) void k_decode_flat(const DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+  __shared__ unsigned long long s_total;
+  __shared__ FlatWalk walk;
+  const int tid = threadIdx.x;
+  const int64_t w = blockIdx.x;
+  if (tid == 0) s_total = 0;
+  __syncthreads();
+  {
+    unsigned long long part = 0;
+    for (int b = tid; b < a.batch; b += kThreads) part += (clamped_len(a, b) + kPage - 1) / kPage;
+    atomicAdd(&s_total, part);
+  }
+  __syncthreads();
+  const int64_t T = (int64_t)uniform64(s_total);
+  // empty sequences own no slots: record (0, 0) for them (strided over workgroups)
+  for (int b = (int)w * kThreads + tid; b < a.batch; b += (int)gridDim.x * kThreads)
+    if (clamped_len(a, b) == 0) {
+      a.meta[2 * b] = 0;
+      a.meta[2 * b + 1] = 0;
+    }
+  const int64_t G = T < (int64_t)gridDim.x ? T : (int64_t)gridDim.x;
+  if (w >= G) return;  // uniform: no share for this workgroup (or no pages at all)
+  if (tid == 0) {
+    walk.start = share_start(w, T, G);
+    walk.end = share_start(w + 1, T, G);
+    walk.next = 0;
+    walk.mask = 0;
+    walk.b0 = -64;
+    walk.j = 64;
+  }
+  for (;;) {
+    __syncthreads();  // walk initialised / every wavefront has read the previous piece
+    if (tid < 64) flat_next_piece(a, walk, w, T, G);
+    __syncthreads();
+    const int b = __builtin_amdgcn_readfirstlane(walk.piece[0]);
+    if (b < 0) return;
+    const int L = __builtin_amdgcn_readfirstlane(walk.piece[1]);
+    const int k0 = __builtin_amdgcn_readfirstlane(walk.piece[2]);
+    const int k1 = __builtin_amdgcn_readfirstlane(walk.piece[3]);
+    process_range<F, false>(a, smem, b, L, k0, k1, w + b);
+  }
+}
+
+// ---------------------------------------------------------------- combine kernels
 // One wavefront per (sequence, head): lane owns channels [8 lane, 8 lane + 8).
 // out = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse); empty splits
 // (lse = -inf) carry no weight and their partial rows are never read.
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_part, const float* __restrict__ lse_part,
-                                                 int H, int S, __bf16* __restrict__ out, float* __restrict__ lse_out) {
-  const int b = blockIdx.y;
-  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
+__device__ __forceinline__ void combine_rows(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                                             int64_t first, int count, int64_t stride_rows, int64_t b, int H, int head,
+                                             __bf16* __restrict__ out, float* __restrict__ lse_out) {
   const int lane = threadIdx.x & 63;
-  if (head >= H) return;
-  const float* lp = lse_part + (int64_t)b * S * H + head;
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[(int64_t)s * H]);
+  for (int s = 0; s < count; ++s) M = fmaxf(M, lse_part[(first + s * stride_rows) * H + head]);
   f32x4 acc0 = {}, acc1 = {};
   float W = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = lp[(int64_t)s * H];
+    for (int s = 0; s < count; ++s) {
+      const int64_t row = (first + s * stride_rows) * H + head;
+      const float ls = lse_part[row];
       if (ls == -INFINITY) continue;
-      const float w = expf(ls - M);
-      W += w;
-      const float* src = o_part + (((int64_t)b * S + s) * H + head) * kDc + 8 * lane;
-      acc0 += w * *(const f32x4*)src;
-      acc1 += w * *(const f32x4*)(src + 4);
+      const float wgt = expf(ls - M);
+      W += wgt;
+      const float* src = o_part + row * kDc + 8 * lane;
+      acc0 += wgt * *(const f32x4*)src;
+      acc1 += wgt * *(const f32x4*)(src + 4);
     }
   }
   const float inv = (M != -INFINITY) ? 1.0f / W : 0.0f;
@@ -639,24 +804,57 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_par
   acc1 *= inv;
   const u32x4 packed = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
                         pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
-  *(u32x4*)(out + ((int64_t)b * H + head) * kDc + 8 * lane) = packed;
+  *(u32x4*)(out + (b * H + head) * kDc + 8 * lane) = packed;
   if (lse_out && lane == 0) lse_out[b * H + head] = (M != -INFINITY) ? M + logf(W) : -INFINITY;
+}
+
+// per-sequence splits: rows (b * S + s) * H + head
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                                                 int H, int S, __bf16* __restrict__ out, float* __restrict__ lse_out) {
+  const int b = blockIdx.y;
+  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (head >= H) return;
+  combine_rows(o_part, lse_part, (int64_t)b * S, S, 1, b, H, head, out, lse_out);
+}
+
+// balanced partition: slots [meta[2b], meta[2b] + meta[2b + 1]) of sequence b
+// (an empty sequence has count 0: output 0, lse -inf)
+__global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part, const int* __restrict__ meta,
+                                                      int H, __bf16* __restrict__ out, float* __restrict__ lse_out) {
+  const int b = blockIdx.y;
+  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (head >= H) return;
+  combine_rows(o_part, lse_part, meta[2 * b], meta[2 * b + 1], 1, b, H, head, out, lse_out);
 }
 
 // ---------------------------------------------------------------- launchers
 
 constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
 
+template <typename K>
+static hipError_t set_lds(K kernel, bool& done) {  // benign race: the attribute is idempotent
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLds);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
 template <int F, bool D>
 static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
-  static bool attr_done = false;  // benign race: the attribute is idempotent
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_decode<F, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kDecodeLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static bool attr_done = false;
+  hipError_t e = set_lds(k_decode<F, D>, attr_done);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_decode<F, D>), dim3(a.num_splits, batch), dim3(kThreads), kDecodeLds, stream, a);
+  return hipGetLastError();
+}
+
+template <int F>
+static hipError_t launch_flat_one(const DecodeArgs& a, int groups, hipStream_t stream) {
+  static bool attr_done = false;
+  hipError_t e = set_lds(k_decode_flat<F>, attr_done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_decode_flat<F>), dim3(groups), dim3(kThreads), kDecodeLds, stream, a);
   return hipGetLastError();
 }
 
@@ -666,10 +864,23 @@ hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, h
   return direct ? launch_one<kBF16, true>(a, batch, stream) : launch_one<kBF16, false>(a, batch, stream);
 }
 
+hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream) {
+  if (fmt == kC4R4) return launch_flat_one<kC4R4>(a, groups, stream);
+  if (fmt == kC2R4) return launch_flat_one<kC2R4>(a, groups, stream);
+  return launch_flat_one<kBF16>(a, groups, stream);
+}
+
 hipError_t launch_combine(const float* o_part, const float* lse_part, int batch, int heads, int splits,
                           __bf16* out, float* lse_out, hipStream_t stream) {
   hipLaunchKernelGGL(k_combine, dim3((heads + 3) / 4, batch), dim3(256), 0, stream, o_part, lse_part, heads, splits,
                      out, lse_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_flat(const float* o_part, const float* lse_part, const int* meta, int batch, int heads,
+                               __bf16* out, float* lse_out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_combine_flat, dim3((heads + 3) / 4, batch), dim3(256), 0, stream, o_part, lse_part, meta,
+                     heads, out, lse_out);
   return hipGetLastError();
 }
 

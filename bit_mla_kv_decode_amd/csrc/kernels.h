@@ -10,6 +10,7 @@ struct DecodeArgs {
   int64_t num_pages;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  int batch;
   int heads;
   int max_pages;
   int num_splits;
@@ -19,11 +20,15 @@ struct DecodeArgs {
   float* lse_part;       // [B][S][H]
   __bf16* out;           // [B][H][512] (direct mode)
   float* lse_out;        // [B][H] or null (direct mode)
+  int* meta;             // balanced partition: [B][first slot, slot count]
 };
 
 hipError_t launch_quant_append(int fmt, const void* latent, const void* rope, const int32_t* slots, int n_new,
                                void* cache, int64_t num_pages, hipStream_t stream);
 hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream);
+hipError_t launch_combine_flat(const float* o_part, const float* lse_part, const int* meta, int batch, int heads,
+                               __bf16* out, float* lse_out, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int batch, int heads, int splits,
                           __bf16* out, float* lse_out, hipStream_t stream);
 

@@ -96,15 +96,19 @@ mla_status_t mla_quant_append(const mla_format_t* fmt,
                               const int32_t* slot_mapping, int32_t n_new,
                               void* cache, int64_t num_pages, void* stream);
 
-/* Split count the library picks for a decode of this shape (num_splits == 0),
- * from the batch size, the longest sequence and the number of compute units;
- * always in [1, 64]. */
+/* A per-sequence split count suited to this shape (from the batch size, the
+ * longest sequence and the number of compute units), for callers that want
+ * the fixed-split mode; always in [1, 64].  num_splits = 0 (the balanced
+ * partition) needs no such choice. */
 int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
                               int32_t max_seq_len);
 
-/* Workspace bytes mla_decode_lowbit / mla_decode_partial need for this shape:
- * fp32 partial outputs [batch, num_splits, num_heads, d_c] followed by fp32
- * partial log-sum-exps [batch, num_splits, num_heads] (256-byte aligned). */
+/* Workspace bytes mla_decode_lowbit / mla_decode_partial need for this shape
+ * (0 for an invalid argument).  num_splits = S >= 1: fp32 partial outputs
+ * [batch, S, num_heads, d_c], then fp32 partial log-sum-exps
+ * [batch, S, num_heads].  num_splits = 0: the same two arrays over
+ * 256 + batch partial slots, then int32 [batch, 2] (first slot, slot count)
+ * per sequence.  Each array starts 256-byte aligned. */
 size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
                                   int32_t num_splits);
 
@@ -122,16 +126,21 @@ size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_
  *                 lse = -inf; values above max_pages_per_seq * page_size are
  *                 clamped to that capacity)
  *   num_heads     1..128
- *   max_seq_len   host upper bound on seq_lens (used to pick num_splits)
- *   num_splits    0 = automatic, else 1..64 contiguous page ranges per
- *                 sequence computed in parallel and merged by log-sum-exp
- *   workspace     >= mla_decode_workspace_bytes(fmt, batch, num_heads, S)
- *                 device bytes (S = the split count used); may be NULL when
- *                 the split count used is 1
+ *   max_pages_per_seq  1..2^24
+ *   max_seq_len   host upper bound on seq_lens (sizes the fixed splits)
+ *   num_splits    0 = balanced: the batch's pages, in sequence order, are cut
+ *                 into min(256, pages) equal shares, one workgroup per share
+ *                 (one per compute unit), whatever the length mix; 1..64 = every
+ *                 sequence cut into that many contiguous page ranges.  Either
+ *                 way the pieces are merged by log-sum-exp
+ *   workspace     >= mla_decode_workspace_bytes(fmt, batch, num_heads,
+ *                 num_splits) device bytes, 256-byte aligned; may be NULL
+ *                 when num_splits is 1
  *   out_bf16      [batch, num_heads, d_c]
  *   lse_out       [batch, num_heads] fp32, or NULL
  * Results do not depend on how pages are placed in the pool, and are
- * bit-identical from run to run for the same split count. */
+ * bit-identical from run to run for the same num_splits and seq_lens (the
+ * balanced cut depends on every sequence's length). */
 mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16,
                                const void* cache, int64_t num_pages,
                                const int32_t* block_table, const int32_t* seq_lens,
@@ -145,11 +154,16 @@ mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16,
  * mla_decode_partial writes, for split s of sequence b, the normalized
  * partial output over that split's pages and its log-sum-exp (-inf for an
  * empty split) into `workspace` (layout of mla_decode_workspace_bytes).
- * mla_decode_combine merges them into out_bf16 / lse_out.  Split s of
- * sequence b covers pages [s * P, (s + 1) * P) with
- * P = ceil(ceil(max_seq_len / page_size) / num_splits), the last split running
- * to the end of the sequence; both stages must be given the same num_splits
- * (the resolved count when 0 was passed: see mla_decode_num_splits). */
+ * mla_decode_combine merges them into out_bf16 / lse_out.  With
+ * num_splits = S >= 1, split s of sequence b covers pages [s * P, (s + 1) * P)
+ * with P = ceil(ceil(max_seq_len / page_size) / S), the last split running to
+ * the end of the sequence.  With num_splits = 0, T = the batch's pages in all
+ * and G = min(256, T), workgroup w < G takes pages
+ * [floor(w * T / G), floor((w + 1) * T / G)) of the concatenation of all
+ * sequences' pages (never empty), writes its piece of sequence b to slot
+ * w + b, and records each sequence's (first slot, slot count) in the
+ * workspace ((0, 0) for an empty sequence).  Both stages
+ * must be given the same num_splits, batch and num_heads. */
 mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16,
                                 const void* cache, int64_t num_pages,
                                 const int32_t* block_table, const int32_t* seq_lens,

@@ -53,7 +53,14 @@ def test_split_heuristic_and_workspace():
         n = B * S * H
         expect = (n * 512 * 4 + 255) // 256 * 256 + (n * 4 + 255) // 256 * 256
         assert mla.mla_decode_workspace_bytes(f, B, H, S) == expect
+    # balanced partition: 256 + B slots, then int32 (first slot, count) per sequence
+    for B, H in [(8, 128), (1, 1), (300, 17)]:
+        n = (256 + B) * H
+        expect = (n * 512 * 4 + 255) // 256 * 256 + (n * 4 + 255) // 256 * 256 + (B * 8 + 255) // 256 * 256
+        assert mla.mla_decode_workspace_bytes(f, B, H, 0) == expect
     assert mla.mla_decode_workspace_bytes(f, 8, 0, 4) == 0
+    assert mla.mla_decode_workspace_bytes(f, 8, 128, -1) == 0
+    assert mla.mla_decode_workspace_bytes(f, 8, 128, 65) == 0
 
 
 def _fmt(name="C4R4"):
@@ -99,6 +106,10 @@ def test_decode_argument_errors():
     assert _decode(splits=4, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
     assert _decode(splits=4, ws=None) == mla.MLA_ERR_INVALID_ARG
     assert _decode(splits=4, ws=ctypes.c_void_p(0x10010)) == mla.MLA_ERR_INVALID_ARG
+    # so does the balanced partition (num_splits = 0)
+    need0 = mla.mla_decode_workspace_bytes("C4R4", 2, 128, 0)
+    assert _decode(splits=0, ws_bytes=need0 - 1) == mla.MLA_ERR_WORKSPACE
+    assert _decode(splits=0, ws=None) == mla.MLA_ERR_INVALID_ARG
     # empty batch: nothing launched
     assert _decode(batch=0, q=None, cache=None, bt=None, sl=None, out=None) == mla.MLA_OK
 
@@ -106,7 +117,10 @@ def test_decode_argument_errors():
 def test_combine_argument_errors():
     L = mla.load_library()
     need = mla.mla_decode_workspace_bytes("C4R4", 2, 8, 3)
-    assert L.mla_decode_combine(_fmt(), 2, 8, 0, A2, need, A, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_combine(_fmt(), 2, 8, -1, A2, need, A, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_combine(_fmt(), 2, 8, 65, A2, need, A, None, None) == mla.MLA_ERR_INVALID_ARG
+    need0 = mla.mla_decode_workspace_bytes("C4R4", 2, 8, 0)
+    assert L.mla_decode_combine(_fmt(), 2, 8, 0, A2, need0 - 1, A, None, None) == mla.MLA_ERR_WORKSPACE
     assert L.mla_decode_combine(_fmt(), 2, 8, 3, A2, need - 4, A, None, None) == mla.MLA_ERR_WORKSPACE
     assert L.mla_decode_combine(_fmt(), 2, 0, 3, A2, need, A, None, None) == mla.MLA_ERR_UNSUPPORTED
     assert L.mla_decode_combine(_fmt(), 2, 8, 3, A2, need, None, None, None) == mla.MLA_ERR_INVALID_ARG

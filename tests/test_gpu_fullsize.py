@@ -1,6 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
-uses (library-chosen split count, partial + combine), checked on sampled
-sequences and heads that the CPU oracle can compute one by one."""
+uses (balanced partition, num_splits = 0, partial + combine), checked on
+sampled sequences and heads that the CPU oracle can compute one by one."""
 import math
 
 import numpy as np
@@ -46,7 +46,7 @@ def _decode(w, fmt, lens, bt, cache):
     B, H = w.batch, w.heads
     q = W.queries(w, "cuda")
     max_len = int(lens.max())
-    S = mla.mla_decode_num_splits(fmt, B, H, max_len)
+    S = 0
     ws = torch.empty(mla.mla_decode_workspace_bytes(fmt, B, H, S), dtype=torch.uint8, device="cuda")
     out = torch.empty(B, H, 512, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B, H, dtype=torch.float32, device="cuda")
@@ -90,7 +90,7 @@ def test_fullsize_sampled(name):
     q, out, lse, S = _decode(w, w.fmt, lens, bt, cache)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     for b in sorted({0, w.batch - 1, int(np.argmax(lens))}):
-        _say("  check sequence %d (L=%d, splits %d)" % (b, int(lens[b]), S))
+        _say("  check sequence %d (L=%d)" % (b, int(lens[b])))
         _check_sequence(w, w.fmt, b, lens, bt, cache, q, out, lse)
     del cache
     torch.cuda.empty_cache()

@@ -143,7 +143,7 @@ def test_decode_matches_oracle(fmt, lens, heads, splits):
     assert_lse(lse, ref_lse)
 
 
-@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("splits", [0, 1, 4])
 def test_empty_sequences(splits):
     fmt = "C4R4"
     w, lens, bt, npages, lat, rope, slots, q = build(fmt, [0, 100, 0, 64], 128, seed=3)
@@ -239,3 +239,74 @@ def test_partial_then_combine_equals_fused():
     fused, flse = gpu_decode(fmt, q, cache, bt, lens, S)
     assert np.array_equal(out.float().cpu().numpy(), fused)
     assert np.array_equal(lse.cpu().numpy(), flse)
+
+
+# ------------------------------------------------------------------ balanced partition
+
+def balanced_pieces(lens, groups=256):
+    """The documented num_splits = 0 cut: T pages in sequence order, G = min(256, T)
+    shares, share w = pages [w T / G, (w + 1) T / G); returns {slot: (b, first page,
+    end page)} and per-sequence (first slot, count)."""
+    n = [(int(L) + 63) // 64 for L in lens]
+    T = sum(n)
+    G = min(groups, T)
+    off = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    pieces, meta = {}, [(0, 0)] * len(lens)
+    for w in range(G):
+        s0, s1 = w * T // G, (w + 1) * T // G
+        for b in range(len(lens)):
+            lo, hi = max(off[b], s0), min(off[b + 1], s1)
+            if lo < hi:
+                pieces[w + b] = (b, int(lo - off[b]), int(hi - off[b]))
+    for b in range(len(lens)):
+        sl = sorted(k for k, v in pieces.items() if v[0] == b)
+        if sl:
+            assert sl == list(range(sl[0], sl[0] + len(sl)))
+            meta[b] = (sl[0], len(sl))
+    return pieces, np.array(meta, dtype=np.int32).reshape(-1, 2)
+
+
+@pytest.mark.parametrize("fmt,lens,heads", [
+    ("C4R4", [100, 0, 700, 5], 128),                               # 14 pages < 256 shares
+    ("C2R4", [0] * 3 + [1, 64, 65, 3000, 129] * 30 + [0, 2000], 16),  # 152 sequences, spans chunks of 64
+    ("BF16", [640, 1, 6000, 70], 40),
+])
+def test_balanced_partition_pieces(fmt, lens, heads):
+    """Every (workgroup, sequence) piece of the balanced partition against the
+    oracle on that piece's pages, the slot records against the documented cut,
+    and the merged output against the oracle."""
+    _say("balanced %s B=%d H=%d" % (fmt, len(lens), heads))
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, lens, heads, seed=len(lens) * 7 + heads)
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    host = cache.cpu().numpy()
+    B, H = len(lens), heads
+    ws = torch.full((mla.mla_decode_workspace_bytes(fmt, B, H, 0),), 0xFF, dtype=torch.uint8, device="cuda")
+    qd, btd, sld = q.cuda(), torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+    mla.mla_decode_partial(fmt, qd, cache, btd, sld, SCALE, 0, ws, max_seq_len=int(lens.max()))
+    out = torch.empty(B, H, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, H, dtype=torch.float32, device="cuda")
+    mla.mla_decode_combine(fmt, B, H, 0, ws, out, lse)
+    torch.cuda.synchronize()
+    o_part, l_part, meta = (t.cpu().numpy() for t in mla.balanced_workspace_views(fmt, ws, B, H))
+    pieces, want_meta = balanced_pieces(lens)
+    assert np.array_equal(meta, want_meta)
+    for slot, (b, p0, p1) in sorted(pieces.items()):
+        ro, rl = oracle.decode(OFMT[fmt], q[b:b + 1], host, npages, bt[b:b + 1], lens[b:b + 1], SCALE,
+                               t_begin=p0 * 64, t_end=p1 * 64)
+        assert np.allclose(o_part[slot], ro[0], rtol=1e-4, atol=1e-4), "slot %d (b=%d pages %d..%d)" % (slot, b, p0, p1)
+        assert np.allclose(l_part[slot], rl[0], rtol=1e-5, atol=1e-4)
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, host, npages, bt, lens, SCALE)
+    assert_close(out.float().cpu().numpy(), ref, "balanced")
+    assert_lse(lse.cpu().numpy(), ref_lse)
+    fused, flse = gpu_decode(fmt, q, cache, bt, lens, 0)
+    assert np.array_equal(out.float().cpu().numpy(), fused) and np.array_equal(lse.cpu().numpy(), flse)
+
+
+def test_balanced_all_empty():
+    fmt = "C4R4"
+    lens = np.zeros(5, np.int32)
+    q = torch.randn(5, 8, 576).to(torch.bfloat16)
+    cache = mla.alloc_cache(fmt, 2)
+    bt = np.zeros((5, 2), np.int32)
+    out, lse = gpu_decode(fmt, q, cache, bt, lens, 0)
+    assert (out == 0).all() and np.isneginf(lse).all()
