@@ -63,6 +63,35 @@ def build_workload(w, device, replicas):
     return lens, bt, npages, caches, q, new_lat, new_rope, new_slots
 
 
+KERNEL_SOURCES = ("bit_mla_kv_decode_amd/csrc/decode.hip", "bit_mla_kv_decode_amd/csrc/common.h",
+                  "bit_mla_kv_decode_amd/csrc/kernels.h")
+
+
+def kernel_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload, fmt):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel sources have
+    changed since the counters were taken."""
+    import re
+    path = os.path.join(ROOT, "profiles", "traffic_k_decode_flat_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
+    val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", txt)
+    if not sha or not val or sha.group(1) != kernel_source_sha256():
+        return None
+    return int(val.group(1))
+
+
 def cpu_baseline(w, seqs=8):
     """Oracle decode (fp64) on the first `seqs` sequences, all heads, on the host cores."""
     import oracle
@@ -82,10 +111,18 @@ def cpu_baseline(w, seqs=8):
     dt = time.perf_counter() - t
     tokens = int(lens.sum())
     from bit_mla_kv_decode_amd import mla_token_bytes
-    gbs = tokens * mla_token_bytes(w.fmt) / dt / 1e9
+    tb = mla_token_bytes(w.fmt)
+    gbs = tokens * tb / dt / 1e9
+    # one thread, on the first 4096 tokens of the first sequence
+    n1 = min(4096, int(lens[0]))
+    t = time.perf_counter()
+    oracle.decode(fmt, q[:1], cache, npages, bt[:1], np.array([n1], np.int32), w.softmax_scale, nthreads=1)
+    dt1 = time.perf_counter() - t
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d sequences (%d tokens), all %d heads, decode only (fp64), %.1f s"
-                      % (len(lens), w.batch, tokens, w.heads, dt)}
+                      % (len(lens), w.batch, tokens, w.heads, dt),
+            "single_thread": {"value": round(n1 * tb / dt1 / 1e9, 6), "unit": "GB/s",
+                              "sample": "%d tokens of one sequence, all heads, %.2f s" % (n1, dt1)}}
 
 
 def main():
@@ -175,8 +212,10 @@ def main():
         bound, achieved, peak, unit = "mfma", k_tflops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", packed_bytes / (k_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    roofline = {"kernel": "k_decode (split-KV partial)", "bound": bound, "achieved": round(achieved, 2),
-                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+    traffic = counted_traffic(w.name, w.fmt) if (S == 0 and not args.heads and not args.format) else None
+    roofline = {"kernel": "k_decode_flat (balanced split-KV partial)" if S == 0 else "k_decode (split-KV partial)",
+                "bound": bound, "achieved": round(achieved, 2),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel_ms": round(k_ms, 4), "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
                 "intensity_flop_per_byte": round(intensity, 1)}
 

@@ -9,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_lowbit.so")
+PEAKS_LIB = os.path.join(PKG, "libmla_peaks.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -24,11 +25,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into bit_mla_kv_decode_amd/libmla_lowbit.so (always rebuilds)."""
+def _hipcc(srcs, lib, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *sources(), "-o", tmp]
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,8 +37,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the decode library (csrc/*.hip -> libmla_lowbit.so) and the
+    practical-peak microbenchmarks (csrc/peaks -> libmla_peaks.so); always rebuilds."""
+    _hipcc(sorted(glob.glob(os.path.join(CSRC, "peaks", "*.hip"))), PEAKS_LIB, verbose)
+    return _hipcc(sources(), LIB, verbose)
 
 
 if __name__ == "__main__":

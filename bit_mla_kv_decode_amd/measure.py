@@ -1,0 +1,313 @@
+"""Measurements of the low-bit MLA decode path on one GPU.
+
+  python -m bit_mla_kv_decode_amd.measure [--only peaks,configs,bf16,heads,pages]
+      JSON lines on stdout, one per measured row (progress on stderr):
+      - peaks:   practical peaks from the microbenchmarks (streaming HBM read,
+                 plain copy, dense bf16 MFMA loop)
+      - configs: every workload: decode partial / combine / append times
+                 (median of per-launch HIP events), packed GB/s, TFLOP/s and
+                 the roofline fraction max(t_HBM, t_MFMA) / t; balanced and
+                 fixed-split partitions
+      - bf16:    the unquantized-cache kernel on the C2R4 workload's data
+      - heads:   head-count sweep at the 8 x 131072 C4R4 shape
+      - pages:   contiguous vs randomly permuted page tables
+  python -m bit_mla_kv_decode_amd.measure --counters
+      the launches a rocprofv3 --pmc run counts: a 1 GiB plain copy three
+      times, then the 8 x 131072 C4R4 decode (bench configuration) three times
+  python -m bit_mla_kv_decode_amd.measure --parse-counters FETCH.csv WRITE.csv
+      per-launch HBM bytes of the decode kernel from FETCH_SIZE / WRITE_SIZE,
+      each scaled by what the counter reads for the copy of known size
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import math
+import sys
+
+import numpy as np
+
+HBM_PEAK = 8.0e12
+MFMA_BF16_PEAK = 2.5e15
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def emit(rec):
+    print(json.dumps(rec), flush=True)
+    return rec
+
+
+def flops_per_token(heads):
+    return 2.0 * heads * (576 + 512)
+
+
+# ------------------------------------------------------------------ timing helpers
+
+def _events(fn, iters, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i + 1)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+class Case:
+    """A workload's caches (replicated past the 256 MB last-level cache) and decode buffers."""
+
+    def __init__(self, w, min_total=1.0e9):
+        import torch
+        import bit_mla_kv_decode_amd as mla
+        from bit_mla_kv_decode_amd import workloads as W
+        self.w = w
+        self.lens = W.seq_lens(w)
+        self.bt, self.npages = W.page_table(w, self.lens)
+        first = mla.alloc_cache(w.fmt, self.npages)
+        hold = w.append_new
+        for b, L in enumerate(self.lens):
+            end = int(L) - 1 if hold else int(L)
+            for t0 in range(0, end, 32768):
+                t1 = min(end, t0 + 32768)
+                lat, rope = W.sequence_rows(w, b, t0, t1, "cuda")
+                mla.mla_quant_append(w.fmt, lat, rope, torch.from_numpy(W.slots_for(self.bt, b, t0, t1)).cuda(), first)
+        self.new_lat, self.new_rope = W.new_token_rows(w, self.lens, "cuda")
+        self.new_slots = torch.from_numpy(np.array([W.slots_for(self.bt, b, int(L) - 1, int(L))[0]
+                                                    for b, L in enumerate(self.lens)], np.int32)).cuda()
+        if hold:
+            mla.mla_quant_append(w.fmt, self.new_lat, self.new_rope, self.new_slots, first)
+        used = int(((self.lens.astype(np.int64) + 63) // 64).sum()) * mla.mla_page_bytes(w.fmt)
+        self.packed = int(self.lens.sum()) * mla.mla_token_bytes(w.fmt)
+        self.pool_bytes = first.numel()
+        reps = max(1, min(12, math.ceil(min_total / max(self.pool_bytes, 1))))
+        self.caches = [first] + [first.clone() for _ in range(reps - 1)]
+        self.used_page_bytes = used
+        self.q = W.queries(w, "cuda")
+        self.btd = torch.from_numpy(self.bt).cuda()
+        self.sld = torch.from_numpy(self.lens).cuda()
+        self.out = torch.empty(w.batch, w.heads, 512, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(w.batch, w.heads, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def time(self, splits=0, iters=20, warmup=5, q=None):
+        import torch
+        import bit_mla_kv_decode_amd as mla
+        w, B = self.w, self.w.batch
+        q = self.q if q is None else q
+        H = int(q.shape[1])
+        out = self.out if H == self.w.heads else torch.empty(B, H, 512, dtype=torch.bfloat16, device="cuda")
+        lse = self.lse if H == self.w.heads else torch.empty(B, H, dtype=torch.float32, device="cuda")
+        ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, H, splits), dtype=torch.uint8, device="cuda")
+        st = torch.cuda.current_stream()
+        R = len(self.caches)
+        mx = int(self.lens.max())
+        part = _events(lambda i: mla.mla_decode_partial(w.fmt, q, self.caches[i % R], self.btd, self.sld,
+                                                          w.softmax_scale, splits, ws, max_seq_len=mx, stream=st),
+                       iters, warmup, st)
+        comb = _events(lambda i: mla.mla_decode_combine(w.fmt, B, H, splits, ws, out, lse, stream=st),
+                       iters, warmup, st)
+        app = _events(lambda i: mla.mla_quant_append(w.fmt, self.new_lat, self.new_rope, self.new_slots,
+                                                      self.caches[i % R], stream=st), iters, warmup, st)
+        return float(np.median(part)), float(np.median(comb)), float(np.median(app))
+
+    def row(self, label, splits=0, q=None, **extra):
+        w = self.w
+        H = w.heads if q is None else int(q.shape[1])
+        tp, tc, ta = self.time(splits, q=q)
+        tok = int(self.lens.sum())
+        fl = tok * flops_per_token(H)
+        t_hbm, t_mfma = self.packed / HBM_PEAK, fl / MFMA_BF16_PEAK
+        return emit({"row": label, "workload": w.name, "format": w.fmt, "batch": w.batch, "heads": H,
+                     "tokens": tok, "pages": w.pages, "partition": "balanced" if splits == 0 else "S=%d" % splits,
+                     "decode_ms": round(tp, 4), "combine_ms": round(tc, 4), "append_ms": round(ta, 4),
+                     "step_ms": round(tp + tc + ta, 4),
+                     "packed_GBps": round(self.packed / (tp * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(self.packed / (tp * 1e-3) / HBM_PEAK, 4),
+                     "TFLOPs": round(fl / (tp * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(fl / (tp * 1e-3) / MFMA_BF16_PEAK, 4),
+                     "roofline_frac": round(max(t_hbm, t_mfma) / (tp * 1e-3), 4),
+                     "bound": "mfma" if t_mfma > t_hbm else "hbm", "replicas": len(self.caches), **extra})
+
+
+# ------------------------------------------------------------------ sections
+
+def section_peaks():
+    import torch
+    from bit_mla_kv_decode_amd import peaks
+    st = torch.cuda.current_stream()
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4096 * 256, dtype=torch.float32, device="cuda")
+    best = 0.0
+    for g in (1024, 2048, 4096):
+        t = _events(lambda i: peaks.read(src, sink, g, st), 10, 2, st)
+        best = max(best, n / (np.median(t) * 1e-3))
+    emit({"row": "peak_hbm_read", "GBps": round(best / 1e9, 1), "frac_of_8TBps": round(best / HBM_PEAK, 4)})
+    t = _events(lambda i: peaks.copy(src, dst, st), 10, 2, st)
+    cp = 2 * n / (np.median(t) * 1e-3)
+    emit({"row": "peak_copy", "GBps_read_plus_write": round(cp / 1e9, 1)})
+    fl = peaks.mfma_bf16(2048, 4000, sink, st)
+    t = _events(lambda i: peaks.mfma_bf16(2048, 4000, sink, st), 5, 1, st)
+    mf = fl / (np.median(t) * 1e-3)
+    emit({"row": "peak_mfma_bf16_32x32x16", "TFLOPs": round(mf / 1e12, 1), "frac_of_2p5PF": round(mf / MFMA_BF16_PEAK, 4)})
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def section_configs():
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    from bit_mla_kv_decode_amd import workloads as W
+    for name in ("tiny_c4r4", "dsv3_c4r4_8k", "c2r4_32k_outliers", "c4r4_128k", "mixed_c2r4_serving"):
+        log("config %s" % name)
+        c = Case(W.WORKLOADS[name])
+        extra = {}
+        if name == "c4r4_128k":
+            extra["compression_vs_bf16"] = round(int(c.lens.sum()) * 1152 / c.used_page_bytes, 3)
+        c.row("config", 0, **extra)
+        S = mla.mla_decode_num_splits(c.w.fmt, c.w.batch, c.w.heads, int(c.lens.max()))
+        c.row("config_fixed_splits", S)
+        del c
+        torch.cuda.empty_cache()
+
+
+def section_bf16():
+    import torch
+    from bit_mla_kv_decode_amd import workloads as W
+    w = W.WORKLOADS["c2r4_32k_outliers"]
+    log("bf16 baseline on %s data" % w.name)
+    c = Case(W.derive(w, fmt="BF16"), min_total=0)
+    c.row("bf16_baseline", 0)
+    del c
+    torch.cuda.empty_cache()
+
+
+def section_heads():
+    import torch
+    from bit_mla_kv_decode_amd import workloads as W
+    w = W.WORKLOADS["c4r4_128k"]
+    log("head sweep on %s" % w.name)
+    c = Case(w)
+    for H in (16, 32, 64, 128):
+        c.row("head_sweep", 0, q=c.q[:, :H].contiguous())
+    del c
+    torch.cuda.empty_cache()
+
+
+def section_pages():
+    import torch
+    from bit_mla_kv_decode_amd import workloads as W
+    for name in ("dsv3_c4r4_8k", "c2r4_32k_outliers", "c4r4_128k"):
+        log("random pages: %s" % name)
+        c = Case(W.derive(W.WORKLOADS[name], pages="random"))
+        c.row("random_pages", 0)
+        del c
+        torch.cuda.empty_cache()
+
+
+SECTIONS = {"peaks": section_peaks, "configs": section_configs, "bf16": section_bf16,
+            "heads": section_heads, "pages": section_pages}
+
+
+# ------------------------------------------------------------------ counters
+
+def run_counters():
+    """The launches one rocprofv3 --pmc pass counts (kernel names tell them apart)."""
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    from bit_mla_kv_decode_amd import peaks
+    from bit_mla_kv_decode_amd import workloads as W
+    st = torch.cuda.current_stream()
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        peaks.copy(src, dst, st)
+    torch.cuda.synchronize()
+    del src, dst
+    log("copy: 3 x %d bytes" % n)
+    c = Case(W.WORKLOADS["c4r4_128k"])
+    w, B, H = c.w, c.w.batch, c.w.heads
+    ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, H, 0), dtype=torch.uint8, device="cuda")
+    for i in range(3):
+        mla.mla_decode_partial(w.fmt, c.q, c.caches[i % len(c.caches)], c.btd, c.sld, w.softmax_scale, 0, ws,
+                               max_seq_len=int(c.lens.max()), stream=st)
+    torch.cuda.synchronize()
+    log("decode: 3 launches, %d packed bytes each, %d replicas" % (c.packed, len(c.caches)))
+    print(json.dumps({"copy_bytes": n, "packed_bytes": c.packed}), flush=True)
+
+
+def _counter_rows(path):
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _is_kernel(name, short):
+    # demangled "(anonymous namespace)::k_copy(...)" / "mla::k_decode_flat<0>(...)",
+    # or mangled "...6k_copy..." / "...13k_decode_flat..."
+    return ("::%s(" % short in name or "::%s<" % short in name or name.startswith(short + "(")
+            or ("%d%s" % (len(short), short)) in name)
+
+
+def _per_dispatch(rows, short, counter):
+    return [v for k, c, v in rows if _is_kernel(k, short) and c == counter]
+
+
+def parse_counters(fetch_csv, write_csv, copy_bytes=1 << 30, packed_bytes=None):
+    """Per-launch HBM bytes of the decode kernel, each counter scaled by its reading on the copy."""
+    fr, wr = _counter_rows(fetch_csv), _counter_rows(write_csv)
+    cf = _per_dispatch(fr, "k_copy", "FETCH_SIZE")
+    cw = _per_dispatch(wr, "k_copy", "WRITE_SIZE")
+    df = _per_dispatch(fr, "k_decode_flat", "FETCH_SIZE")
+    dw = _per_dispatch(wr, "k_decode_flat", "WRITE_SIZE")
+    if not (cf and cw and df and dw):
+        raise SystemExit("counter files lack the copy or decode dispatches")
+    f_scale = copy_bytes / float(np.median(cf))   # bytes per counted unit (nominally 1024)
+    w_scale = copy_bytes / float(np.median(cw))
+    rec = {"copy_FETCH_SIZE": float(np.median(cf)), "copy_WRITE_SIZE": float(np.median(cw)),
+           "fetch_scale_bytes_per_unit": round(f_scale, 2), "write_scale_bytes_per_unit": round(w_scale, 2),
+           "decode_FETCH_SIZE": [round(v, 1) for v in df], "decode_WRITE_SIZE": [round(v, 1) for v in dw],
+           "decode_read_bytes": int(np.median(df) * f_scale), "decode_write_bytes": int(np.median(dw) * w_scale)}
+    rec["decode_traffic_bytes"] = rec["decode_read_bytes"] + rec["decode_write_bytes"]
+    if packed_bytes:
+        rec["read_over_packed"] = round(rec["decode_read_bytes"] / packed_bytes, 4)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--only", default=",".join(SECTIONS))
+    ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--parse-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--packed-bytes", type=int, default=None)
+    args = ap.parse_args()
+    if args.parse_counters:
+        print(json.dumps(parse_counters(*args.parse_counters, packed_bytes=args.packed_bytes)))
+        return
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    if not torch.cuda.is_available():
+        raise SystemExit("measure needs a GPU")
+    mla.load_library()
+    if args.counters:
+        run_counters()
+        return
+    for s in args.only.split(","):
+        SECTIONS[s]()
+
+
+if __name__ == "__main__":
+    main()

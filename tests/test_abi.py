@@ -17,10 +17,10 @@ A = ctypes.c_void_p(0x10000)
 A2 = ctypes.c_void_p(0x20000)
 
 
-def _declared():
-    txt = open(HEADER).read()
+def _declared(header=HEADER, prefix="mla_"):
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(%s[a-z0-9_]+)\s*\(" % prefix, txt)))
 
 
 def test_header_symbols_are_exported():
@@ -29,6 +29,19 @@ def test_header_symbols_are_exported():
     assert {"mla_quant_append", "mla_decode_lowbit", "mla_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_peaks_header_symbols_are_exported():
+    from bit_mla_kv_decode_amd import peaks
+    lib = peaks.load_library()
+    names = _declared(os.path.join(ROOT, "include", "mla_peaks.h"), "peak_")
+    assert names == ["peak_copy", "peak_mfma_bf16", "peak_read"]
+    for n in names:
+        assert hasattr(lib, n), n
+    # host-side argument checks (no launch): misaligned or ragged sizes are refused
+    assert lib.peak_copy(A, A2, 17, None) != 0
+    assert lib.peak_read(A, 1000, 256, A2, None) != 0
+    assert lib.peak_mfma_bf16(0, 10, A2, None) != 0
 
 
 def test_format_queries():
