@@ -6,24 +6,26 @@
 //   S[h, t] = scale * <q[h, 0:576], khat[t, 0:576]>       (latent + RoPE key)
 //   O[h, :] = sum_t softmax_t(S[h, :]) * khat[t, 0:512]   (latent is the value)
 //
-// One workgroup = one (split, sequence) pair, 256 threads = 4 wavefronts, one
-// per SIMD.  Wave w owns heads [32w, 32w + 32).  The work is tiled by half
-// pages (32 tokens):
+// One workgroup = one piece of work (a page range of one sequence: a fixed
+// split, or a share of the balanced partition), 256 threads = 4 wavefronts,
+// one per SIMD.  Wave w owns heads [32w, 32w + 32) (for <= 32 heads the four
+// wavefronts split the channels of one head group instead, see
+// split_pass_cs).  The work is tiled by half pages (32 tokens):
 //   1. fill: every thread loads its share of the next tile's packed bytes
 //      (16-byte loads; the 32 lanes of a half-wave read 512 contiguous bytes of
 //      one code chunk), dequantizes them in registers once for all heads
 //      (bf16(fma(code, S, Z))) and writes a bf16 tile khat[32][576] to LDS
-//      (rows padded to 1168 bytes).  Tiles are double
-//      buffered, so the loads of tile k+1 are in flight while tile k computes.
-//   2. Q.K^T on MFMA 32x32x16 bf16: A = khat rows (ds_read_b128), B = q^T held
-//      in registers for the whole split (32 heads x 576 = 144 VGPRs), giving
+//      (rows padded to 1168 bytes).  Tiles are double buffered, so the loads
+//      of tile k+1 are in flight while tile k computes.
+//   2. Q.K^T on MFMA 32x32x16 bf16: A = khat rows (ds_read_b128), B = q^T
+//      (half of the k-steps staged in LDS, half in registers), giving
 //      S^T[token][head]: each lane holds one head and 16 tokens per block.
 //   3. softmax weights in registers: per-head max over the lane's tokens, the
 //      other half-wave via v_permlane32_swap; exp2 with the scale folded into
-//      log2 units.  Weights are taken against a fixed reference per split (the
-//      first tile's max), so O is never rescaled and stays in the MFMA
-//      accumulators; a split whose logits rise more than 2^64 above that
-//      reference is recomputed with its true max (see split_pass).
+//      log2 units.  Weights are taken against a fixed reference per piece (the
+//      first tile's max, lifted), so O is never rescaled and stays in the MFMA
+//      accumulators; a piece whose logits rise beyond the reference's range
+//      is recomputed with its true max (see split_pass).
 //   4. P.V on MFMA 32x32x16 bf16 with the latent as value: A = khat^T read
 //      with ds_read_b64_tr_b16 (transposing 16-bit loads) from the same tile,
 //      B = P straight from the softmax registers.  P is split into a bf16 high
@@ -31,9 +33,9 @@
 //      ~16 significant bits; a single bf16 P loses too much accuracy when a few
 //      tokens with large, cancelling latent values dominate a head.
 //      O^T[channel][head] accumulates in 256 fp32 registers per lane.
-//   5. per split: O / l and lse = m + log l are written as fp32 partials (or,
+//   5. per piece: O / l and lse = m + log l are written as fp32 partials (or,
 //      with one split, the final bf16 output directly).
-// A second kernel merges the splits with log-sum-exp weights.
+// A second kernel merges the pieces with log-sum-exp weights.
 #include "kernels.h"
 
 namespace mla {
@@ -300,12 +302,15 @@ struct PageWindow {
     const int lane = threadIdx.x & 63;
     ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
   }
+  // The lane read sits in both branches, so the wait for a window load stays
+  // on the (rare) refill path instead of draining every load in flight.
   __device__ __forceinline__ int page_of(int kt) {
     const int pg = kt >> 1;
     if (pg - wbase >= 64) {  // uniform; once per 64 pages
       wbase = pg;
       const int lane = threadIdx.x & 63;
       ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
+      return __builtin_amdgcn_readlane(ids, 0);
     }
     return __builtin_amdgcn_readlane(ids, pg - wbase);
   }
@@ -492,6 +497,220 @@ __device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16
   }
 }
 
+// ---------------------------------------------------------------- channel-split variant
+// For num_heads <= 32 one head group per wavefront would leave three
+// wavefronts (SIMDs) without MFMA work, and one tile in flight per compute
+// unit keeps HBM far from busy.  Here the 4 wavefronts form 4 / C head groups
+// of C wavefronts (the launcher uses C = 4 for <= 32 heads); part c of a group takes
+// k-steps [c NK, (c + 1) NK) of Q.K^T (NK = 36 / C, q entirely in registers)
+// and channels [c 512 / C, (c + 1) 512 / C) of P.V (O in 256 / C
+// accumulators).  The partial logits go through LDS; every wavefront of the
+// group adds the C parts in the same order, so all of them hold bitwise the
+// same S, weights and denominator.  The freed registers hold the packed bytes
+// of D tiles ahead instead of one.
+template <int C> struct CsAcc {
+  f32x16 o[16 / C];
+  float l_sum, m_ref, m_seen;
+};
+
+constexpr int kXchFloats = 64 * 16;  // one wavefront's partial S^T block
+
+template <int F, int C, int D>
+__device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int k0,
+                                              int k1, const bf16x8 (&qr)[36 / C], bool fixed, float m_fixed,
+                                              CsAcc<C>& acc) {
+  constexpr int NK = 36 / C, NCT = 16 / C;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5;
+  const int part = wave % C, group = wave / C;
+  float* xch = (float*)(smem + 2 * kTile);  // [wave][4][lane][4] floats
+  const int g = lane >> 4, i16 = lane & 15;
+  const int tr_row0 = 4 * (i16 >> 2) + (g >> 1);
+  const int tr_chunk = 2 * (g & 1) + ((i16 & 3) >> 1);
+  const int tr_half = 4 * (i16 & 1);
+
+#pragma unroll
+  for (int i = 0; i < NCT; ++i) acc.o[i] = (f32x16){};
+  acc.l_sum = 0.0f;
+  acc.m_ref = fixed ? m_fixed : -INFINITY;
+  acc.m_seen = -INFINITY;
+  bool lifted = false;
+
+  PageWindow win(bt, k0, k1);
+  {
+    Fill<F> first;
+    first.load(a.cache, win.page_of(k0), k0 & 1, a.num_pages);
+    first.store(smem, min(kTileTok, L - k0 * kTileTok));
+  }
+  // ring: fr[j] holds the packed bytes of tile k + 1 while tile k (k - k0 = j
+  // mod D) computes; tiles past the range reload the last one (harmless)
+  Fill<F> fr[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int kt = min(k0 + 1 + j, k1 - 1);
+    fr[j].load(a.cache, win.page_of(kt), kt & 1, a.num_pages);
+  }
+  __syncthreads();
+
+  for (int kb = k0; kb < k1; kb += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int k = kb + j;
+      if (k >= k1) break;  // uniform
+      __bf16* tile = smem + ((k - k0) & 1) * kTile;
+      __bf16* next = smem + ((k - k0 + 1) & 1) * kTile;
+      const int nvalid = min(kTileTok, L - k * kTileTok);
+      // ---- partial S^T over this part's k-steps, operands read 4 ahead
+      f32x16 s = {};
+      const __bf16* arow = tile + rho(lane & 31) * kRow + 8 * hi + 16 * (part * NK);
+      bf16x8 kv[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) kv[d] = *(const bf16x8*)(arow + 16 * d);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[i & 3], qr[i], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 4 < NK) kv[i & 3] = *(const bf16x8*)(arow + 16 * (i + 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- sum the group's C parts in part order
+      {
+        float* xw = xch + wave * kXchFloats + 4 * lane;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) *(f32x4*)(xw + 256 * j4) = (f32x4){s[4 * j4], s[4 * j4 + 1], s[4 * j4 + 2], s[4 * j4 + 3]};
+        __syncthreads();
+        const float* xg = xch + group * C * kXchFloats + 4 * lane;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          f32x4 v = *(const f32x4*)(xg + 256 * j4);
+#pragma unroll
+          for (int p = 1; p < C; ++p) v += *(const f32x4*)(xg + p * kXchFloats + 256 * j4);
+          s[4 * j4] = v[0];
+          s[4 * j4 + 1] = v[1];
+          s[4 * j4 + 2] = v[2];
+          s[4 * j4 + 3] = v[3];
+        }
+      }
+      // ---- softmax weights, as in split_pass
+      if (nvalid < kTileTok) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[r] = -INFINITY;
+      }
+      if (k == k0 && !fixed) {
+        float smax = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
+        acc.m_ref = fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift;
+      }
+      const float neg_ref = -acc.m_ref;
+      float ps = 0.0f;
+      unsigned phi[8], plo[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, neg_ref));
+        const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.scale_log2, neg_ref));
+        ps += pa + pb;
+        const unsigned h2 = pack_bf16x2(pa, pb);
+        phi[r >> 1] = h2;
+        plo[r >> 1] = pack_bf16x2(pa - bf16_lo(h2), pb - bf16_hi(h2));
+      }
+      {
+        float smax = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
+        const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
+        acc.m_seen = fmaxf(acc.m_seen, mt);
+        lifted |= mt - acc.m_ref > kMaxLift;
+      }
+      acc.l_sum += ps;
+      // ---- O^T (this part's channels) += khat^T . P, next tile's dequant between the MFMAs
+      const int nvalid_next = min(kTileTok, L - (k + 1) * kTileTok);
+      constexpr int kSub = Fill<F>::kSubsteps;
+      constexpr int kSlots = 4 * NCT;                        // MFMAs of this phase
+      constexpr int kPer = kSub ? (kSub + kSlots - 1) / kSlots : 1;  // dequant steps per MFMA slot
+      constexpr int kFirst = kSlots - (kSub + kPer - 1) / kPer;     // first slot that carries steps
+      bf16x8 bp[2][2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bp[kk][0] = __builtin_bit_cast(bf16x8, (u32x4){phi[4 * kk], phi[4 * kk + 1], phi[4 * kk + 2], phi[4 * kk + 3]});
+        bp[kk][1] = __builtin_bit_cast(bf16x8, (u32x4){plo[4 * kk], plo[4 * kk + 1], plo[4 * kk + 2], plo[4 * kk + 3]});
+      }
+      const __bf16* vbase = tile + tr_row0 * kRow + 8 * tr_chunk + tr_half + 32 * (part * NCT);
+      auto tr_read = [&](int step) {  // step = NCT kk + ct (ct relative to this part)
+        const __bf16* v0 = vbase + 16 * (step / NCT) * kRow + 32 * (step % NCT);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v0);
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + 2 * kRow));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 va[3];
+#pragma unroll
+      for (int d = 0; d < 3; ++d) va[d] = tr_read(d);
+#pragma unroll
+      for (int step = 0; step < 2 * NCT; ++step) {
+        const int kk = step / NCT, ct = step % NCT;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          __builtin_amdgcn_sched_barrier(0);
+          acc.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % 3], bp[kk][h], acc.o[ct], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          const int slot = 2 * step + h - kFirst;
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            const int u = slot * kPer + e;
+            if (slot >= 0 && u < kSub) fr[j].substep(next, nvalid_next, u);
+          }
+        }
+        if (step + 3 < 2 * NCT) va[step % 3] = tr_read(step + 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kSub == 0) fr[j].store(next, nvalid_next);
+      // the ring slot is free again: packed bytes of tile k + 1 + D
+      {
+        const int kt = min(k + 1 + D, k1 - 1);
+        fr[j].load(a.cache, win.page_of(kt), kt & 1, a.num_pages);
+      }
+      __syncthreads();
+    }
+  }
+  return lifted;
+}
+
+template <bool kDirect, int C>
+__device__ __forceinline__ void write_split_cs(const DecodeArgs& a, int b, int64_t slot, int head, const CsAcc<C>& acc) {
+  constexpr int NCT = 16 / C;
+  const int hi = (threadIdx.x & 63) >> 5, part = (threadIdx.x >> 6) % C;
+  const float l_tot = acc.l_sum + wave_partner(acc.l_sum);
+  const float inv = 1.0f / l_tot;
+  const float lse = (acc.m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+  const int H = a.heads;
+  if (head >= H) return;
+  if (kDirect) {
+    __bf16* orow = a.out + ((int64_t)b * H + head) * kDc + 4 * hi + 32 * (part * NCT);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const unsigned w0 = pack_bf16x2(acc.o[ct][4 * rq] * inv, acc.o[ct][4 * rq + 1] * inv);
+        const unsigned w1 = pack_bf16x2(acc.o[ct][4 * rq + 2] * inv, acc.o[ct][4 * rq + 3] * inv);
+        *(uint2*)(orow + 32 * ct + 8 * rq) = make_uint2(w0, w1);
+      }
+    if (a.lse_out && hi == 0 && part == 0) a.lse_out[b * H + head] = lse;
+  } else {
+    const int64_t row = slot * H + head;
+    float* orow = a.o_part + row * kDc + 4 * hi + 32 * (part * NCT);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x4 v = {acc.o[ct][4 * rq] * inv, acc.o[ct][4 * rq + 1] * inv, acc.o[ct][4 * rq + 2] * inv,
+                         acc.o[ct][4 * rq + 3] * inv};
+        *(f32x4*)(orow + 32 * ct + 8 * rq) = v;
+      }
+    if (hi == 0 && part == 0) a.lse_part[row] = lse;
+  }
+}
+
 // Writes one pass result: the final bf16 output (direct mode) or an fp32
 // partial row at a.o_part[row * 512] / a.lse_part[row] (row = slot * H + head).
 template <bool kDirect>
@@ -530,7 +749,7 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t 
 
 // Attention of sequence b over its tiles [k0, k1) (non-empty), written to
 // `slot`.  Called by every thread of the workgroup (uniform control flow).
-template <int F, bool kDirect>
+template <int F, bool kDirect, int C>
 __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem, int b, int L, int k0, int k1,
                                               int64_t slot) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -538,58 +757,89 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem,
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
   __syncthreads();  // the previous range (if any) has finished with LDS
-  // stage the LDS k-steps of q (zeros for heads >= H): LDS chunk c of head h
-  // holds channels 16 (2 (c / 2)) + 8 (c % 2) + [0, 8); the first tile's
-  // barrier publishes it
-  {
-    __bf16* ql = smem + 2 * kTile;
-    for (int ci = tid; ci < 128 * (kQLds / 8); ci += kThreads) {
-      const int h = ci / (kQLds / 8), c = ci % (kQLds / 8);
-      bf16x8 v = {};
-      if (h < H) v = *(const bf16x8*)(a.q + ((int64_t)b * H + h) * kD + 32 * (c >> 1) + 8 * (c & 1));
-      *(bf16x8*)(ql + h * kQRow + 8 * c) = v;
-    }
-  }
-
-  if (wave * 32 >= H) {  // no heads for this wavefront: fill only (uniform per wave)
-    for (int pass = 0;; ++pass) {
-      split_pass_fill_only<F>(a, smem, bt, L, k0, k1);
-      const bool redo = __syncthreads_or(0);
-      if (!redo || pass > 0) return;
-    }
-  }
-
-  const int head = wave * 32 + (lane & 31);
-  const int hi = lane >> 5;
-  // q^T operand: lane holds head `head`, channels 16 ks + 8 hi + [0, 8) of the
-  // register k-steps (odd ks < 32, and 32..35); the even ks < 32 are in LDS
-  bf16x8 qr[kQRegSteps];
-  {
-    const int hq = head < H ? head : H - 1;
-    const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi;
-    const bf16x8 zero = {};
+  if constexpr (C > 1) {
+    // channel split: every wavefront has heads (the launcher picks C from H)
+    constexpr int NK = 36 / C;
+    const int part = wave % C, group = wave / C;
+    const int head = group * 32 + (lane & 31), hi = lane >> 5;
+    bf16x8 qr[NK];
+    {
+      const int hq = head < H ? head : H - 1;
+      const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi + 16 * (part * NK);
+      const bf16x8 zero = {};
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-      if (q_in_lds(ks)) continue;
-      const bf16x8 v = *(const bf16x8*)(qh + 16 * ks);
-      qr[q_reg_index(ks)] = head < H ? v : zero;
+      for (int i = 0; i < NK; ++i) {
+        const bf16x8 v = *(const bf16x8*)(qh + 16 * i);
+        qr[i] = head < H ? v : zero;
+      }
     }
-  }
-  // pass 0 takes the first tile's max (plus kRefLift) as reference; a second
-  // pass (only when a logit rises more than kRefLift + kMaxLift above that
-  // max) uses the split's true max found by pass 0.
-  bool fixed = false;
-  float m_fixed = 0.0f;
-  for (int pass = 0;; ++pass) {
-    SplitAcc acc;
-    const bool lifted = split_pass<F>(a, smem, bt, L, k0, k1, qr, fixed, m_fixed, acc);
-    const bool redo = __syncthreads_or(lifted);
-    if (!redo || pass > 0) {
-      write_split<kDirect>(a, b, slot, head, acc);
-      return;
+    bool fixed = false;
+    float m_fixed = 0.0f;
+    for (int pass = 0;; ++pass) {
+      CsAcc<C> acc;
+      const bool lifted = split_pass_cs<F, C, 3>(a, smem, bt, L, k0, k1, qr, fixed, m_fixed, acc);
+      const bool redo = __syncthreads_or(lifted);
+      if (!redo || pass > 0) {
+        write_split_cs<kDirect, C>(a, b, slot, head, acc);
+        return;
+      }
+      fixed = true;
+      m_fixed = acc.m_seen;
     }
-    fixed = true;
-    m_fixed = acc.m_seen;
+  } else {
+    // stage the LDS k-steps of q (zeros for heads >= H): LDS chunk c of head h
+    // holds channels 16 (2 (c / 2)) + 8 (c % 2) + [0, 8); the first tile's
+    // barrier publishes it
+    {
+      __bf16* ql = smem + 2 * kTile;
+      for (int ci = tid; ci < 128 * (kQLds / 8); ci += kThreads) {
+        const int h = ci / (kQLds / 8), c = ci % (kQLds / 8);
+        bf16x8 v = {};
+        if (h < H) v = *(const bf16x8*)(a.q + ((int64_t)b * H + h) * kD + 32 * (c >> 1) + 8 * (c & 1));
+        *(bf16x8*)(ql + h * kQRow + 8 * c) = v;
+      }
+    }
+
+    if (wave * 32 >= H) {  // no heads for this wavefront: fill only (uniform per wave)
+      for (int pass = 0;; ++pass) {
+        split_pass_fill_only<F>(a, smem, bt, L, k0, k1);
+        const bool redo = __syncthreads_or(0);
+        if (!redo || pass > 0) return;
+      }
+    }
+
+    const int head = wave * 32 + (lane & 31);
+    const int hi = lane >> 5;
+    // q^T operand: lane holds head `head`, channels 16 ks + 8 hi + [0, 8) of the
+    // register k-steps (odd ks < 32, and 32..35); the even ks < 32 are in LDS
+    bf16x8 qr[kQRegSteps];
+    {
+      const int hq = head < H ? head : H - 1;
+      const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi;
+      const bf16x8 zero = {};
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) {
+        if (q_in_lds(ks)) continue;
+        const bf16x8 v = *(const bf16x8*)(qh + 16 * ks);
+        qr[q_reg_index(ks)] = head < H ? v : zero;
+      }
+    }
+    // pass 0 takes the first tile's max (plus kRefLift) as reference; a second
+    // pass (only when a logit rises more than kRefLift + kMaxLift above that
+    // max) uses the split's true max found by pass 0.
+    bool fixed = false;
+    float m_fixed = 0.0f;
+    for (int pass = 0;; ++pass) {
+      SplitAcc acc;
+      const bool lifted = split_pass<F>(a, smem, bt, L, k0, k1, qr, fixed, m_fixed, acc);
+      const bool redo = __syncthreads_or(lifted);
+      if (!redo || pass > 0) {
+        write_split<kDirect>(a, b, slot, head, acc);
+        return;
+      }
+      fixed = true;
+      m_fixed = acc.m_seen;
+    }
   }
 }
 
@@ -600,7 +850,7 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
 
 // Per-sequence splits: workgroup (split, b) covers pages [split * P, (split + 1) * P)
 // of sequence b, the last split running to the end of the sequence.
-template <int F, bool kDirect>
+template <int F, bool kDirect, int C>
 __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   const int split = blockIdx.x, b = blockIdx.y;
@@ -620,7 +870,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
     return;
   }
   // tiles are half pages: tile k covers tokens [32 k, 32 k + 32)
-  process_range<F, kDirect>(a, smem, b, L, 2 * p0, min(2 * p1, (L + kTileTok - 1) / kTileTok),
+  process_range<F, kDirect, C>(a, smem, b, L, 2 * p0, min(2 * p1, (L + kTileTok - 1) / kTileTok),
                             (int64_t)b * a.num_splits + split);
 }
 
@@ -730,7 +980,7 @@ __device__ __forceinline__ void flat_next_piece(const DecodeArgs& a, FlatWalk& w
   }
 }
 
-template <int F>
+template <int F, int C>
 __global__ __launch_bounds__(kThreads, 1) void k_decode_flat(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   __shared__ unsigned long long s_total;
@@ -771,7 +1021,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_flat(const DecodeArgs a)
     const int L = __builtin_amdgcn_readfirstlane(walk.piece[1]);
     const int k0 = __builtin_amdgcn_readfirstlane(walk.piece[2]);
     const int k1 = __builtin_amdgcn_readfirstlane(walk.piece[3]);
-    process_range<F, false>(a, smem, b, L, k0, k1, w + b);
+    process_range<F, false, C>(a, smem, b, L, k0, k1, w + b);
   }
 }
 
@@ -840,34 +1090,55 @@ static hipError_t set_lds(K kernel, bool& done) {  // benign race: the attribute
   return e;
 }
 
-template <int F, bool D>
+// Channel split by head count for the quantized formats: all 4 wavefronts on
+// one group of <= 32 heads, else one head group per wavefront (the
+// unquantized baseline always uses the latter).  Measured on 8 x 131072 C4R4
+// tokens: 16-32 heads 0.31 -> 0.26 ms; a 2-way split at 64 heads was slower
+// than one group per wavefront, so it is not used.
+static int channel_split(int fmt, int heads) {
+  if (fmt == kBF16) return 1;
+  return heads <= 32 ? 4 : 1;
+}
+
+template <int F, bool D, int C>
 static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
   static bool attr_done = false;
-  hipError_t e = set_lds(k_decode<F, D>, attr_done);
+  hipError_t e = set_lds(k_decode<F, D, C>, attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode<F, D>), dim3(a.num_splits, batch), dim3(kThreads), kDecodeLds, stream, a);
+  hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch), dim3(kThreads), kDecodeLds, stream, a);
   return hipGetLastError();
 }
 
-template <int F>
+template <int F, int C>
 static hipError_t launch_flat_one(const DecodeArgs& a, int groups, hipStream_t stream) {
   static bool attr_done = false;
-  hipError_t e = set_lds(k_decode_flat<F>, attr_done);
+  hipError_t e = set_lds(k_decode_flat<F, C>, attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_flat<F>), dim3(groups), dim3(kThreads), kDecodeLds, stream, a);
+  hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups), dim3(kThreads), kDecodeLds, stream, a);
   return hipGetLastError();
+}
+
+template <int F, int C>
+static hipError_t launch_split(bool direct, const DecodeArgs& a, int batch, hipStream_t stream) {
+  return direct ? launch_one<F, true, C>(a, batch, stream) : launch_one<F, false, C>(a, batch, stream);
 }
 
 hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream) {
-  if (fmt == kC4R4) return direct ? launch_one<kC4R4, true>(a, batch, stream) : launch_one<kC4R4, false>(a, batch, stream);
-  if (fmt == kC2R4) return direct ? launch_one<kC2R4, true>(a, batch, stream) : launch_one<kC2R4, false>(a, batch, stream);
-  return direct ? launch_one<kBF16, true>(a, batch, stream) : launch_one<kBF16, false>(a, batch, stream);
+  const int c = channel_split(fmt, a.heads);
+  if (fmt == kC4R4)
+    return c == 4 ? launch_split<kC4R4, 4>(direct, a, batch, stream) : launch_split<kC4R4, 1>(direct, a, batch, stream);
+  if (fmt == kC2R4)
+    return c == 4 ? launch_split<kC2R4, 4>(direct, a, batch, stream) : launch_split<kC2R4, 1>(direct, a, batch, stream);
+  return launch_split<kBF16, 1>(direct, a, batch, stream);
 }
 
 hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream) {
-  if (fmt == kC4R4) return launch_flat_one<kC4R4>(a, groups, stream);
-  if (fmt == kC2R4) return launch_flat_one<kC2R4>(a, groups, stream);
-  return launch_flat_one<kBF16>(a, groups, stream);
+  const int c = channel_split(fmt, a.heads);
+  if (fmt == kC4R4)
+    return c == 4 ? launch_flat_one<kC4R4, 4>(a, groups, stream) : launch_flat_one<kC4R4, 1>(a, groups, stream);
+  if (fmt == kC2R4)
+    return c == 4 ? launch_flat_one<kC2R4, 4>(a, groups, stream) : launch_flat_one<kC2R4, 1>(a, groups, stream);
+  return launch_flat_one<kBF16, 1>(a, groups, stream);
 }
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int batch, int heads, int splits,

@@ -310,3 +310,19 @@ def test_balanced_all_empty():
     bt = np.zeros((5, 2), np.int32)
     out, lse = gpu_decode(fmt, q, cache, bt, lens, 0)
     assert (out == 0).all() and np.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4"])
+@pytest.mark.parametrize("heads", [1, 16, 31, 32, 33, 63, 64, 65, 100])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_head_counts(fmt, heads, splits):
+    """Every head-count regime of the decode: 4, 2 or 1 wavefronts per
+    32-head group (channel split), with ragged lengths and a partial tile."""
+    _say("heads %s H=%d S=%d" % (fmt, heads, splits))
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, [1500, 70, 0, 333], heads, seed=heads + 17,
+                                                     outliers=fmt == "C2R4")
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    out, lse = gpu_decode(fmt, q, cache, bt, lens, splits)
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, cache.cpu().numpy(), npages, bt, lens, SCALE)
+    assert_close(out, ref, "%s H=%d S=%d" % (fmt, heads, splits))
+    assert_lse(lse, ref_lse)
