@@ -407,12 +407,14 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
       for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
       acc.m_ref = fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift;
     }
-    // the weights need only the fixed reference, not this tile's max
+    // the weights need only the fixed reference, not this tile's max.  Regs
+    // r < 8 are the tokens of P.V k-step 0 (tokens 0..15): those weights come
+    // first; the rest (and the max tracking) are computed between the MFMAs
+    // of k-step 0.
     const float neg_ref = -acc.m_ref;
     float ps = 0.0f;
     unsigned phi[8], plo[8];  // packed bf16 pairs: P high part and remainder
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
+    auto weights = [&](int r) {
       // v_exp_f32 directly: weights below 2^-126 of the reference flush to 0
       const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, neg_ref));
       const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.scale_log2, neg_ref));
@@ -420,33 +422,31 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
       const unsigned h2 = pack_bf16x2(pa, pb);
       phi[r >> 1] = h2;
       plo[r >> 1] = pack_bf16x2(pa - bf16_lo(h2), pb - bf16_hi(h2));
-    }
+    };
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) weights(r);
     // this tile's max (log2 units): tracks the split's true max and detects a
     // rise beyond 2^kMaxLift above the reference (the weights above may then
     // have overflowed: the pass is redone with the true max)
-    {
+    auto track_max = [&]() {
       float smax = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
       const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
       acc.m_seen = fmaxf(acc.m_seen, mt);
       lifted |= mt - acc.m_ref > kMaxLift;
-    }
-    acc.l_sum += ps;
+    };
     // ---- O^T += khat^T . P  (k-step kk covers tile tokens 16 kk .. 16 kk + 15);
     //      the next tile's dequantization pieces are spread between the MFMAs
     const int nvalid_next = min(kTileTok, L - (k + 1) * kTileTok);
     constexpr int kSub = Fill<F>::kSubsteps;
     bf16x8 bp[2][2];  // [kk][hi/lo]
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bp[kk][0] = __builtin_bit_cast(bf16x8, (u32x4){phi[4 * kk], phi[4 * kk + 1], phi[4 * kk + 2], phi[4 * kk + 3]});
-      bp[kk][1] = __builtin_bit_cast(bf16x8, (u32x4){plo[4 * kk], plo[4 * kk + 1], plo[4 * kk + 2], plo[4 * kk + 3]});
-    }
+    bp[0][0] = __builtin_bit_cast(bf16x8, (u32x4){phi[0], phi[1], phi[2], phi[3]});
+    bp[0][1] = __builtin_bit_cast(bf16x8, (u32x4){plo[0], plo[1], plo[2], plo[3]});
     // step = 16 kk + ct: A operand = khat^T for channels [32 ct, 32 ct + 32) and
     // the 16 tokens of k-step kk, read 3 steps ahead.  Scheduling fences pin
-    // the order MFMA / dequantization step / MFMA / ..., so that the VALU work
-    // for the next tile issues in the shadow of the matrix pipe.
+    // the order MFMA / VALU piece / MFMA / ..., so that the VALU work issues in
+    // the shadow of the matrix pipe.
     const __bf16* vbase = tile + tr_row0 * kRow + 8 * tr_chunk + tr_half;
     auto tr_read = [&](int step) {
       const __bf16* v0 = vbase + 16 * (step >> 4) * kRow + 32 * (step & 15);
@@ -460,16 +460,24 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
 #pragma unroll
     for (int step = 0; step < 32; ++step) {
       const int kk = step >> 4, ct = step & 15;
+      if (step == 16) {
+        bp[1][0] = __builtin_bit_cast(bf16x8, (u32x4){phi[4], phi[5], phi[6], phi[7]});
+        bp[1][1] = __builtin_bit_cast(bf16x8, (u32x4){plo[4], plo[5], plo[6], plo[7]});
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         __builtin_amdgcn_sched_barrier(0);
         acc.o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % 3], bp[kk][h], acc.o[ct], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        const int u = 2 * step + h - (64 - kSub);   // dequantization steps in the last kSub slots
+        const int slot = 2 * step + h;
+        if (slot < 4) weights(8 + 2 * slot);       // weights of k-step 1
+        if (slot == 5) track_max();
+        const int u = slot - (64 - kSub);   // dequantization steps in the last kSub slots
         if (u >= 0 && u < kSub) fill.substep(next, nvalid_next, u);
       }
       if (step + 3 < 32) va[step % 3] = tr_read(step + 3);
     }
+    acc.l_sum += ps;
     __builtin_amdgcn_sched_barrier(0);
     if (kSub == 0) fill.store(next, nvalid_next);
     __syncthreads();
@@ -1038,15 +1046,37 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ o_part, c
   f32x4 acc0 = {}, acc1 = {};
   float W = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < count; ++s) {
-      const int64_t row = (first + s * stride_rows) * H + head;
-      const float ls = lse_part[row];
-      if (ls == -INFINITY) continue;
-      const float wgt = expf(ls - M);
-      W += wgt;
-      const float* src = o_part + row * kDc + 8 * lane;
-      acc0 += wgt * *(const f32x4*)src;
-      acc1 += wgt * *(const f32x4*)(src + 4);
+    // four slots' rows in flight at a time; rows of empty pieces (lse = -inf)
+    // are never read (they may hold anything)
+    for (int s0 = 0; s0 < count; s0 += 4) {
+      f32x4 x0[4], x1[4];
+      float wgt[4];
+      bool use[4];
+      int64_t rows[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = s0 + j;
+        rows[j] = (first + s * stride_rows) * H + head;
+        const float ls = s < count ? lse_part[rows[j]] : -INFINITY;
+        use[j] = ls != -INFINITY;
+        wgt[j] = use[j] ? expf(ls - M) : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x0[j] = x1[j] = (f32x4){};
+        if (use[j]) {  // uniform over the wavefront
+          const float* src = o_part + rows[j] * kDc + 8 * lane;
+          x0[j] = *(const f32x4*)src;
+          x1[j] = *(const f32x4*)(src + 4);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (use[j]) {
+          W += wgt[j];
+          acc0 += wgt[j] * x0[j];
+          acc1 += wgt[j] * x1[j];
+        }
     }
   }
   const float inv = (M != -INFINITY) ? 1.0f / W : 0.0f;
