@@ -1,11 +1,13 @@
 """Benchmark: low-bit MLA decode serving step on one MI355X.
 
 One step = the whole hot path over one batch:
-  1. mla_quant_append: quantize + pack the new token of every sequence
-     (position L_b - 1) into the paged cache;
-  2. mla_decode_partial: split-KV attention over the packed cache, the
-     batch's pages cut into one equal share per compute unit (num_splits = 0);
-  3. mla_decode_combine: log-sum-exp merge of the pieces.
+  1. mla_decode_append_partial: the new token of every sequence (position
+     L_b - 1) is quantized and packed into the paged cache by the decode
+     kernel's workgroup that reads that page, then split-KV attention runs
+     over the packed cache, the batch's pages cut into one equal share per
+     compute unit (num_splits = 0);
+  2. mla_decode_combine: log-sum-exp merge of the pieces.
+With --unfused the append is a separate mla_quant_append launch.
 The default workload is the long-context C4R4 decode: 8 sequences x 131072
 tokens, 128 heads (d_c = 512 latent + d_r = 64 RoPE key), 64-token pages.
 Inputs are synthetic and resident in HBM before timing; the cache is
@@ -136,6 +138,7 @@ def main():
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count (head sweep)")
     ap.add_argument("--format", default="", help="override the cache format: C4R4, C2R4 or BF16 (same data)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="separate append launch before the decode")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -181,11 +184,16 @@ def main():
 
     def step(i, timed=None):
         c = caches[i % replicas]
-        mla.mla_quant_append(w.fmt, new_lat, new_rope, new_slots, c, stream=stream)
+        if args.unfused:
+            mla.mla_quant_append(w.fmt, new_lat, new_rope, new_slots, c, stream=stream)
         if timed is not None:
             timed[0].record(stream)
-        mla.mla_decode_partial(w.fmt, q, c, bt_d, sl_d, w.softmax_scale, S, ws, max_seq_len=max_len,
-                               stream=stream)
+        if args.unfused:
+            mla.mla_decode_partial(w.fmt, q, c, bt_d, sl_d, w.softmax_scale, S, ws, max_seq_len=max_len,
+                                   stream=stream)
+        else:
+            mla.mla_decode_append_partial(w.fmt, new_lat, new_rope, q, c, bt_d, sl_d, w.softmax_scale, S, ws,
+                                          max_seq_len=max_len, stream=stream)
         if timed is not None:
             timed[1].record(stream)
         mla.mla_decode_combine(w.fmt, B, H, S, ws, out, lse, stream=stream)
@@ -212,8 +220,10 @@ def main():
         bound, achieved, peak, unit = "mfma", k_tflops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", packed_bytes / (k_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    traffic = counted_traffic(w.name, w.fmt) if (S == 0 and not args.heads and not args.format) else None
-    roofline = {"kernel": "k_decode_flat (balanced split-KV partial)" if S == 0 else "k_decode (split-KV partial)",
+    traffic = (counted_traffic(w.name, w.fmt) if (S == 0 and not args.heads and not args.format and not args.unfused)
+               else None)
+    roofline = {"kernel": ("k_decode_flat (balanced split-KV partial" if S == 0 else "k_decode (split-KV partial") +
+                          (")" if args.unfused else ", fused append)"),
                 "bound": bound, "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel_ms": round(k_ms, 4), "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
@@ -241,7 +251,8 @@ def main():
         "config": {"workload": w.name, "format": w.fmt, "batch": B, "heads": H, "ctx": max_len,
                    "tokens": tokens, "page_size": 64, "cache_replicas": replicas,
                    "partition": "balanced (256 equal page shares)" if S == 0 else "%d splits per sequence" % S,
-                   "step": "quant_append(1 token/seq) + split-KV decode + LSE combine",
+                   "step": ("quant_append(1 token/seq) + split-KV decode + LSE combine" if args.unfused else
+                            "fused append(1 token/seq) + split-KV decode, then LSE combine"),
                    "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,

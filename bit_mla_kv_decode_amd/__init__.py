@@ -16,6 +16,7 @@ __all__ = [
     "FORMATS", "MlaError", "format_struct", "load_library",
     "mla_token_bytes", "mla_page_bytes", "mla_quant_append", "mla_decode_num_splits",
     "mla_decode_workspace_bytes", "mla_decode_lowbit", "mla_decode_partial", "mla_decode_combine",
+    "mla_decode_append_lowbit", "mla_decode_append_partial",
     "mla_last_error", "alloc_cache",
 ]
 
@@ -70,6 +71,10 @@ def load_library():
         "mla_decode_lowbit": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P, P, P]),
         "mla_decode_partial": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P]),
         "mla_decode_combine": (ctypes.c_int, [FP, I32, I32, I32, P, SZ, P, P, P]),
+        "mla_decode_append_lowbit": (ctypes.c_int, [FP, P, P, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ,
+                                                    P, P, P]),
+        "mla_decode_append_partial": (ctypes.c_int, [FP, P, P, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ,
+                                                     P]),
         "mla_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -188,6 +193,50 @@ def mla_decode_lowbit(fmt, q, cache, block_table, seq_lens, softmax_scale, max_s
         _opt(workspace, "workspace", torch.uint8), workspace.numel() if workspace is not None else 0,
         _dev(out, "out", torch.bfloat16), _opt(lse, "lse", torch.float32), _stream(stream)))
     return out, lse
+
+
+def mla_decode_append_lowbit(fmt, latent_new, rope_new, q, cache, block_table, seq_lens, softmax_scale,
+                             max_seq_len=None, num_splits=0, out=None, lse=None, workspace=None, num_pages=None,
+                             stream=None):
+    """The serving step in one call: row b of latent_new [B, 512] / rope_new [B, 64] (bf16) is
+    appended at position seq_lens[b] - 1, then decode over all seq_lens[b] tokens; returns
+    (out, lse) as mla_decode_lowbit.  `cache` is written."""
+    import torch
+    B, H, MP, NP = _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
+    if tuple(latent_new.shape) != (B, 512) or tuple(rope_new.shape) != (B, 64):
+        raise ValueError("latent_new [B, 512] and rope_new [B, 64] expected")
+    if max_seq_len is None:
+        max_seq_len = MP * 64
+    S = int(num_splits)
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    if workspace is None and S != 1:
+        workspace = torch.empty(mla_decode_workspace_bytes(fmt, B, H, S), dtype=torch.uint8, device=q.device)
+    _check(load_library().mla_decode_append_lowbit(
+        ctypes.byref(format_struct(fmt)), _dev(latent_new, "latent_new", torch.bfloat16),
+        _dev(rope_new, "rope_new", torch.bfloat16), _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.uint8),
+        NP, _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
+        int(max_seq_len), float(softmax_scale), S,
+        _opt(workspace, "workspace", torch.uint8), workspace.numel() if workspace is not None else 0,
+        _dev(out, "out", torch.bfloat16), _opt(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse
+
+
+def mla_decode_append_partial(fmt, latent_new, rope_new, q, cache, block_table, seq_lens, softmax_scale, num_splits,
+                              workspace, max_seq_len=None, num_pages=None, stream=None) -> None:
+    """First stage of mla_decode_append_lowbit (append + partial results); complete with mla_decode_combine."""
+    import torch
+    B, H, MP, NP = _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
+    if tuple(latent_new.shape) != (B, 512) or tuple(rope_new.shape) != (B, 64):
+        raise ValueError("latent_new [B, 512] and rope_new [B, 64] expected")
+    if max_seq_len is None:
+        max_seq_len = MP * 64
+    _check(load_library().mla_decode_append_partial(
+        ctypes.byref(format_struct(fmt)), _dev(latent_new, "latent_new", torch.bfloat16),
+        _dev(rope_new, "rope_new", torch.bfloat16), _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.uint8),
+        NP, _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
+        int(max_seq_len), float(softmax_scale), int(num_splits), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream)))
 
 
 def mla_decode_partial(fmt, q, cache, block_table, seq_lens, softmax_scale, num_splits, workspace,

@@ -150,6 +150,95 @@ mla::DecodeArgs make_args(const void* q, const void* cache, int64_t num_pages, c
   return a;
 }
 
+// New-token rows for the fused append, or none.
+struct Append {
+  const void* latent = nullptr;
+  const void* rope = nullptr;
+  void* cache = nullptr;
+};
+
+void set_append(mla::DecodeArgs& a, const Append& ap) {
+  a.new_latent = (const __bf16*)ap.latent;
+  a.new_rope = (const __bf16*)ap.rope;
+  a.append_cache = (uint8_t*)ap.cache;
+}
+
+mla_status_t decode_partial(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,
+                            const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                            int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                            void* workspace, size_t ws_bytes, const Append& ap, void* stream) {
+  DecodeShape sh;
+  mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                 max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
+  if (st != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (!workspace || !aligned(workspace, 256))
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+  if (ws_bytes < workspace_bytes(batch, num_heads, sh.splits))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                workspace_bytes(batch, num_heads, sh.splits));
+  mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                max_pages_per_seq, softmax_scale, sh, workspace);
+  set_append(a, ap);
+  hipError_t e = sh.splits > 0 ? mla::launch_decode(sh.fmt, false, a, batch, (hipStream_t)stream)
+                               : mla::launch_decode_flat(sh.fmt, a, kFlatGroups, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status_t decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits,
+                            const void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out, void* stream) {
+  if (format_id(fmt) < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
+  if (batch < 0 || batch > 65535) return fail(MLA_ERR_INVALID_ARG, "batch must be in 0..65535");
+  if (num_heads < 1 || num_heads > 128) return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128");
+  if (num_splits < 0 || num_splits > kMaxSplits) return fail(MLA_ERR_INVALID_ARG, "num_splits must be in 0..64");
+  if (batch == 0) return MLA_OK;
+  if (!workspace || !out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(workspace, 256) || !aligned(out_bf16, 16) || (lse_out && !aligned(lse_out, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "misaligned workspace or output");
+  if (ws_bytes < workspace_bytes(batch, num_heads, num_splits))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                workspace_bytes(batch, num_heads, num_splits));
+  const float* o_part = (const float*)workspace;
+  const float* lse_part = (const float*)((const char*)workspace + partial_o_bytes(batch, num_heads, num_splits));
+  const int* meta = (const int*)((const char*)lse_part + partial_lse_bytes(batch, num_heads, num_splits));
+  hipError_t e = num_splits > 0
+                     ? mla::launch_combine(o_part, lse_part, batch, num_heads, num_splits, (__bf16*)out_bf16, lse_out,
+                                           (hipStream_t)stream)
+                     : mla::launch_combine_flat(o_part, lse_part, meta, batch, num_heads, (__bf16*)out_bf16, lse_out,
+                                                (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status_t decode_full(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                         int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                         void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out, const Append& ap,
+                         void* stream) {
+  DecodeShape sh;
+  mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                 max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
+  if (st != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MLA_ERR_INVALID_ARG, "out must be a 16-byte aligned pointer");
+  if (lse_out && !aligned(lse_out, 4)) return fail(MLA_ERR_INVALID_ARG, "lse_out must be 4-byte aligned");
+  if (sh.splits == 1) {
+    mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                  max_pages_per_seq, softmax_scale, sh, nullptr);
+    a.out = (__bf16*)out_bf16;
+    a.lse_out = lse_out;
+    set_append(a, ap);
+    hipError_t e = mla::launch_decode(sh.fmt, true, a, batch, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return MLA_OK;
+  }
+  st = decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+                      max_seq_len, softmax_scale, sh.splits, workspace, ws_bytes, ap, stream);
+  if (st != MLA_OK) return st;
+  return decode_combine(fmt, batch, num_heads, sh.splits, workspace, ws_bytes, out_bf16, lse_out, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,48 +283,14 @@ mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16, con
                                 int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
                                 float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
                                 void* stream) {
-  DecodeShape sh;
-  mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
-                                 max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
-  if (st != MLA_OK) return st;
-  if (batch == 0) return MLA_OK;
-  if (!workspace || !aligned(workspace, 256))
-    return fail(MLA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
-  if (ws_bytes < workspace_bytes(batch, num_heads, sh.splits))
-    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
-                workspace_bytes(batch, num_heads, sh.splits));
-  mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
-                                max_pages_per_seq, softmax_scale, sh, workspace);
-  hipError_t e = sh.splits > 0 ? mla::launch_decode(sh.fmt, false, a, batch, (hipStream_t)stream)
-                               : mla::launch_decode_flat(sh.fmt, a, kFlatGroups, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-  return MLA_OK;
+  return decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+                        max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, Append{}, stream);
 }
 
 mla_status_t mla_decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits,
                                 const void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out,
                                 void* stream) {
-  if (format_id(fmt) < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
-  if (batch < 0 || batch > 65535) return fail(MLA_ERR_INVALID_ARG, "batch must be in 0..65535");
-  if (num_heads < 1 || num_heads > 128) return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128");
-  if (num_splits < 0 || num_splits > kMaxSplits) return fail(MLA_ERR_INVALID_ARG, "num_splits must be in 0..64");
-  if (batch == 0) return MLA_OK;
-  if (!workspace || !out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
-  if (!aligned(workspace, 256) || !aligned(out_bf16, 16) || (lse_out && !aligned(lse_out, 4)))
-    return fail(MLA_ERR_INVALID_ARG, "misaligned workspace or output");
-  if (ws_bytes < workspace_bytes(batch, num_heads, num_splits))
-    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
-                workspace_bytes(batch, num_heads, num_splits));
-  const float* o_part = (const float*)workspace;
-  const float* lse_part = (const float*)((const char*)workspace + partial_o_bytes(batch, num_heads, num_splits));
-  const int* meta = (const int*)((const char*)lse_part + partial_lse_bytes(batch, num_heads, num_splits));
-  hipError_t e = num_splits > 0
-                     ? mla::launch_combine(o_part, lse_part, batch, num_heads, num_splits, (__bf16*)out_bf16, lse_out,
-                                           (hipStream_t)stream)
-                     : mla::launch_combine_flat(o_part, lse_part, meta, batch, num_heads, (__bf16*)out_bf16, lse_out,
-                                                (hipStream_t)stream);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
-  return MLA_OK;
+  return decode_combine(fmt, batch, num_heads, num_splits, workspace, ws_bytes, out_bf16, lse_out, stream);
 }
 
 mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,
@@ -243,26 +298,46 @@ mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16, cons
                                int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
                                float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
                                void* out_bf16, float* lse_out, void* stream) {
-  DecodeShape sh;
-  mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
-                                 max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
-  if (st != MLA_OK) return st;
-  if (batch == 0) return MLA_OK;
-  if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MLA_ERR_INVALID_ARG, "out must be a 16-byte aligned pointer");
-  if (lse_out && !aligned(lse_out, 4)) return fail(MLA_ERR_INVALID_ARG, "lse_out must be 4-byte aligned");
-  if (sh.splits == 1) {
-    mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
-                                  max_pages_per_seq, softmax_scale, sh, nullptr);
-    a.out = (__bf16*)out_bf16;
-    a.lse_out = lse_out;
-    hipError_t e = mla::launch_decode(sh.fmt, true, a, batch, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-    return MLA_OK;
+  return decode_full(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+                     max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, out_bf16, lse_out, Append{}, stream);
+}
+
+mla_status_t mla_decode_append_partial(const mla_format_t* fmt, const void* latent_new_bf16,
+                                       const void* rope_new_bf16, const void* q_bf16, void* cache, int64_t num_pages,
+                                       const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                       int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
+                                       float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
+                                       void* stream) {
+  if (batch > 0) {
+    if (!latent_new_bf16 || !rope_new_bf16) return fail(MLA_ERR_INVALID_ARG, "null new-row pointer");
+    if (!aligned(latent_new_bf16, 16) || !aligned(rope_new_bf16, 16))
+      return fail(MLA_ERR_INVALID_ARG, "new latent and rope rows must be 16-byte aligned");
   }
-  st = mla_decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
-                          max_seq_len, softmax_scale, sh.splits, workspace, ws_bytes, stream);
-  if (st != MLA_OK) return st;
-  return mla_decode_combine(fmt, batch, num_heads, sh.splits, workspace, ws_bytes, out_bf16, lse_out, stream);
+  Append ap;
+  ap.latent = latent_new_bf16;
+  ap.rope = rope_new_bf16;
+  ap.cache = cache;
+  return decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+                        max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, ap, stream);
+}
+
+mla_status_t mla_decode_append_lowbit(const mla_format_t* fmt, const void* latent_new_bf16, const void* rope_new_bf16,
+                                      const void* q_bf16, void* cache, int64_t num_pages, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                      int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale,
+                                      int32_t num_splits, void* workspace, size_t ws_bytes, void* out_bf16,
+                                      float* lse_out, void* stream) {
+  if (batch > 0) {
+    if (!latent_new_bf16 || !rope_new_bf16) return fail(MLA_ERR_INVALID_ARG, "null new-row pointer");
+    if (!aligned(latent_new_bf16, 16) || !aligned(rope_new_bf16, 16))
+      return fail(MLA_ERR_INVALID_ARG, "new latent and rope rows must be 16-byte aligned");
+  }
+  Append ap;
+  ap.latent = latent_new_bf16;
+  ap.rope = rope_new_bf16;
+  ap.cache = cache;
+  return decode_full(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+                     max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, out_bf16, lse_out, ap, stream);
 }
 
 }  // extern "C"

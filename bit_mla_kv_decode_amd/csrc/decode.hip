@@ -36,6 +36,7 @@
 //   5. per piece: O / l and lse = m + log l are written as fp32 partials (or,
 //      with one split, the final bf16 output directly).
 // A second kernel merges the pieces with log-sum-exp weights.
+#include "append.h"
 #include "kernels.h"
 
 namespace mla {
@@ -764,6 +765,16 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem,
   const int H = a.heads;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
+  // fused append: the piece holding the sequence's last tile writes the new
+  // token (position L - 1) first; the fence and the barrier below order the
+  // write before any load of that page (no wavefront has read it yet)
+  if (a.new_latent && k1 == (L + kTileTok - 1) / kTileTok && wave == 0) {
+    const int64_t page = bt[(L - 1) / kPage];
+    if (page >= 0 && page < a.num_pages)
+      append_row<F>(a.new_latent + (int64_t)b * kDc, a.new_rope + (int64_t)b * kDr,
+                    a.append_cache + page * (int64_t)PageLayout<F>::kBytes, (L - 1) % kPage);
+    __threadfence();
+  }
   __syncthreads();  // the previous range (if any) has finished with LDS
   if constexpr (C > 1) {
     // channel split: every wavefront has heads (the launcher picks C from H)

@@ -21,6 +21,11 @@ struct DecodeArgs {
   __bf16* out;           // [B][H][512] (direct mode)
   float* lse_out;        // [B][H] or null (direct mode)
   int* meta;             // balanced partition: [B][first slot, slot count]
+  // fused append (null when not fused): row b is quantized into position
+  // seq_lens[b] - 1 of sequence b before that position is read
+  const __bf16* new_latent;  // [B][512]
+  const __bf16* new_rope;    // [B][64]
+  uint8_t* append_cache;     // the cache (writable alias of `cache`)
 };
 
 hipError_t launch_quant_append(int fmt, const void* latent, const void* rope, const int32_t* slots, int n_new,

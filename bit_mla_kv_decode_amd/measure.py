@@ -13,7 +13,8 @@
       - pages:   contiguous vs randomly permuted page tables
   python -m bit_mla_kv_decode_amd.measure --counters
       the launches a rocprofv3 --pmc run counts: a 1 GiB plain copy three
-      times, then the 8 x 131072 C4R4 decode (bench configuration) three times
+      times, then the 8 x 131072 C4R4 decode (bench configuration: fused append +
+      balanced partial) three times
   python -m bit_mla_kv_decode_amd.measure --parse-counters FETCH.csv WRITE.csv
       per-launch HBM bytes of the decode kernel from FETCH_SIZE / WRITE_SIZE,
       each scaled by what the counter reads for the copy of known size
@@ -239,9 +240,9 @@ def run_counters():
     c = Case(W.WORKLOADS["c4r4_128k"])
     w, B, H = c.w, c.w.batch, c.w.heads
     ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, H, 0), dtype=torch.uint8, device="cuda")
-    for i in range(3):
-        mla.mla_decode_partial(w.fmt, c.q, c.caches[i % len(c.caches)], c.btd, c.sld, w.softmax_scale, 0, ws,
-                               max_seq_len=int(c.lens.max()), stream=st)
+    for i in range(3):  # the bench step's decode launch: fused append + balanced partial
+        mla.mla_decode_append_partial(w.fmt, c.new_lat, c.new_rope, c.q, c.caches[i % len(c.caches)], c.btd, c.sld,
+                                      w.softmax_scale, 0, ws, max_seq_len=int(c.lens.max()), stream=st)
     torch.cuda.synchronize()
     log("decode: 3 launches, %d packed bytes each, %d replicas" % (c.packed, len(c.caches)))
     print(json.dumps({"copy_bytes": n, "packed_bytes": c.packed}), flush=True)

@@ -149,6 +149,38 @@ mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16,
                                void* workspace, size_t workspace_bytes,
                                void* out_bf16, float* lse_out, void* stream);
 
+/* The serving step fused into one call: for every sequence b with
+ * seq_lens[b] >= 1, row b of latent_new_bf16 [batch, d_c] and rope_new_bf16
+ * [batch, d_r] is quantized and packed into position seq_lens[b] - 1 (page
+ * block_table[b, (seq_lens[b] - 1) / page_size], offset (seq_lens[b] - 1) %
+ * page_size), then the decode of mla_decode_lowbit runs over all seq_lens[b]
+ * tokens, the new one included.  The result (cache bytes, out, lse) is
+ * identical to mla_quant_append with those slots followed by
+ * mla_decode_lowbit with the same arguments.  The append is done inside the
+ * decode kernel by the workgroup that reads the sequence's last page, so the
+ * new row makes no separate trip.  A page id outside [0, num_pages) skips
+ * the append (as mla_quant_append skips such slots).  Both row pointers must
+ * be 16-byte aligned; `cache` is written. */
+mla_status_t mla_decode_append_lowbit(const mla_format_t* fmt, const void* latent_new_bf16,
+                                      const void* rope_new_bf16, const void* q_bf16, void* cache,
+                                      int64_t num_pages, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                      int32_t max_pages_per_seq, int32_t max_seq_len,
+                                      float softmax_scale, int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* out_bf16, float* lse_out,
+                                      void* stream);
+
+/* The first stage of mla_decode_append_lowbit (append + partial results);
+ * mla_decode_combine completes it.  Arguments as mla_decode_append_lowbit
+ * and mla_decode_partial. */
+mla_status_t mla_decode_append_partial(const mla_format_t* fmt, const void* latent_new_bf16,
+                                       const void* rope_new_bf16, const void* q_bf16, void* cache,
+                                       int64_t num_pages, const int32_t* block_table,
+                                       const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                       int32_t max_pages_per_seq, int32_t max_seq_len,
+                                       float softmax_scale, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* The two stages of mla_decode_lowbit, for callers that schedule them
  * separately (for example to merge partial results computed elsewhere).
  * mla_decode_partial writes, for split s of sequence b, the normalized

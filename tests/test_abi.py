@@ -146,3 +146,21 @@ def test_python_binding_refuses_host_tensors():
     with pytest.raises(TypeError):
         mla.mla_quant_append("C4R4", x, torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(4, dtype=torch.int32),
                              torch.zeros(20736, dtype=torch.uint8))
+
+
+def test_fused_append_argument_errors():
+    L = mla.load_library()
+    A3 = ctypes.c_void_p(0x30000)
+
+    def call(lat=A3, rope=A3, batch=2, splits=0, ws_bytes=1 << 30):
+        return L.mla_decode_append_lowbit(_fmt(), lat, rope, A, A, 10, A, A, batch, 128, 4, 256, 0.07, splits, A2,
+                                          ws_bytes, A, None, None)
+    assert call(lat=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(rope=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(lat=ctypes.c_void_p(0x30008)) == mla.MLA_ERR_INVALID_ARG
+    assert "aligned" in mla.mla_last_error()
+    assert call(ws_bytes=10) == mla.MLA_ERR_WORKSPACE
+    assert call(splits=65) == mla.MLA_ERR_INVALID_ARG
+    assert call(batch=0, lat=None, rope=None) == mla.MLA_OK
+    assert L.mla_decode_append_partial(_fmt(), None, A3, A, A, 10, A, A, 2, 128, 4, 256, 0.07, 0, A2, 1 << 30,
+                                       None) == mla.MLA_ERR_INVALID_ARG

@@ -107,3 +107,33 @@ def test_fullsize_bf16_baseline_on_c2r4_data():
         _check_sequence(w, "BF16", b, lens, bt, cache, q, out, lse)
     del cache
     torch.cuda.empty_cache()
+
+
+def test_fullsize_fused_serving_step():
+    """The mixed serving batch through the fused append + decode (bench's step):
+    the appended rows land bit-exact and sampled outputs match the oracle."""
+    w = W.WORKLOADS["mixed_c2r4_serving"]
+    _say("full-size fused step on %s" % w.name)
+    lens = W.seq_lens(w)
+    bt, npages = W.page_table(w, lens)
+    cache = mla.alloc_cache(w.fmt, npages)
+    for b, L in enumerate(lens):
+        for t0 in range(0, int(L) - 1, 32768):
+            t1 = min(int(L) - 1, t0 + 32768)
+            lat, rope = W.sequence_rows(w, b, t0, t1, "cuda")
+            mla.mla_quant_append(w.fmt, lat, rope, torch.from_numpy(W.slots_for(bt, b, t0, t1)).cuda(), cache)
+    new_lat, new_rope = W.new_token_rows(w, lens, "cuda")
+    q = W.queries(w, "cuda")
+    B, H = w.batch, w.heads
+    lse = torch.empty(B, H, dtype=torch.float32, device="cuda")
+    out, _ = mla.mla_decode_append_lowbit(w.fmt, new_lat, new_rope, q, cache, torch.from_numpy(bt).cuda(),
+                                          torch.from_numpy(lens).cuda(), w.softmax_scale,
+                                          max_seq_len=int(lens.max()), lse=lse)
+    torch.cuda.synchronize()
+    outn, lsen = out.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(outn).all() and np.isfinite(lsen).all()
+    for b in sorted({0, B - 1, int(np.argmin(lens))}):
+        _say("  check sequence %d (L=%d)" % (b, int(lens[b])))
+        _check_sequence(w, w.fmt, b, lens, bt, cache, q.cpu(), outn, lsen)
+    del cache
+    torch.cuda.empty_cache()

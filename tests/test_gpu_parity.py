@@ -326,3 +326,51 @@ def test_head_counts(fmt, heads, splits):
     ref, ref_lse = oracle.decode(OFMT[fmt], q, cache.cpu().numpy(), npages, bt, lens, SCALE)
     assert_close(out, ref, "%s H=%d S=%d" % (fmt, heads, splits))
     assert_lse(lse, ref_lse)
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "BF16"])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("heads", [16, 64])
+def test_fused_append_decode_equals_separate(fmt, splits, heads):
+    """mla_decode_append_lowbit == mla_quant_append of the new rows (at position
+    L - 1) followed by mla_decode_lowbit: same cache bytes, bitwise the same
+    output and LSE; and the output matches the oracle on that cache."""
+    lens = [1, 64, 65, 300, 0, 1000, 129]
+    _say("fused append %s S=%d H=%d" % (fmt, splits, heads))
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, lens, heads, seed=splits + heads, outliers=fmt == "C2R4")
+    # rows of every token except each sequence's last; the last rows are the new ones
+    keep, last_rows = [], []
+    off = 0
+    for b, L in enumerate(lens):
+        L = int(L)
+        keep.extend(range(off, off + max(L - 1, 0)))
+        last_rows.append(off + L - 1 if L > 0 else -1)
+        off += L
+    keep = np.array(keep, dtype=np.int64)
+    base = gpu_cache(fmt, npages, lat[keep], rope[keep], slots[keep])
+    B = len(lens)
+    new_lat = torch.zeros(B, 512, dtype=torch.bfloat16)
+    new_rope = torch.zeros(B, 64, dtype=torch.bfloat16)
+    new_slots = np.full(B, -1, np.int32)
+    for b, r in enumerate(last_rows):
+        if r >= 0:
+            new_lat[b], new_rope[b], new_slots[b] = lat[r], rope[r], slots[r]
+    qd, btd, sld = q.cuda(), torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+    # separate
+    c1 = base.clone()
+    mla.mla_quant_append(fmt, new_lat.cuda(), new_rope.cuda(), torch.from_numpy(new_slots).cuda(), c1)
+    l1 = torch.empty(B, heads, dtype=torch.float32, device="cuda")
+    o1, _ = mla.mla_decode_lowbit(fmt, qd, c1, btd, sld, SCALE, max_seq_len=int(lens.max()), num_splits=splits, lse=l1)
+    # fused
+    c2 = base.clone()
+    l2 = torch.empty(B, heads, dtype=torch.float32, device="cuda")
+    o2, _ = mla.mla_decode_append_lowbit(fmt, new_lat.cuda(), new_rope.cuda(), qd, c2, btd, sld, SCALE,
+                                         max_seq_len=int(lens.max()), num_splits=splits, lse=l2)
+    torch.cuda.synchronize()
+    h1, h2 = c1.cpu().numpy(), c2.cpu().numpy()
+    assert np.array_equal(h1, h2), "%d cache bytes differ" % int((h1 != h2).sum())
+    assert np.array_equal(h2, oracle_cache(fmt, npages, lat, rope, slots))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, h2, npages, bt, lens, SCALE)
+    assert_close(o2.float().cpu().numpy(), ref, "fused %s" % fmt)
+    assert_lse(l2.cpu().numpy(), ref_lse)
