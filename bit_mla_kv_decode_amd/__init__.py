@@ -16,7 +16,8 @@ __all__ = [
     "FORMATS", "MlaError", "format_struct", "load_library",
     "mla_token_bytes", "mla_page_bytes", "mla_quant_append", "mla_decode_num_splits",
     "mla_decode_workspace_bytes", "mla_decode_lowbit", "mla_decode_partial", "mla_decode_combine",
-    "mla_decode_append_lowbit", "mla_decode_append_partial",
+    "mla_decode_append_lowbit", "mla_decode_append_partial", "mla_decode_multi_lowbit",
+    "mla_decode_multi_partial",
     "mla_last_error", "alloc_cache",
 ]
 
@@ -75,6 +76,10 @@ def load_library():
                                                     P, P, P]),
         "mla_decode_append_partial": (ctypes.c_int, [FP, P, P, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ,
                                                      P]),
+        "mla_decode_multi_lowbit": (ctypes.c_int, [FP, P, I32, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ,
+                                                   P, P, P]),
+        "mla_decode_multi_partial": (ctypes.c_int, [FP, P, I32, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ,
+                                                    P]),
         "mla_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -235,6 +240,55 @@ def mla_decode_append_partial(fmt, latent_new, rope_new, q, cache, block_table, 
         ctypes.byref(format_struct(fmt)), _dev(latent_new, "latent_new", torch.bfloat16),
         _dev(rope_new, "rope_new", torch.bfloat16), _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.uint8),
         NP, _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
+        int(max_seq_len), float(softmax_scale), int(num_splits), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream)))
+
+
+def _multi_shapes(q, cache, block_table, seq_lens, fmt, num_pages):
+    if q.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("q [B, s_q, H, 576], block_table [B, max_pages] and seq_lens [B] expected")
+    B, s_q, H, D = (int(v) for v in q.shape)
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("batch sizes of q, block_table and seq_lens differ")
+    pb = mla_page_bytes(fmt)
+    if num_pages is None:
+        num_pages = cache.numel() // pb if pb else 0
+    return B, s_q, H, int(block_table.shape[1]), int(num_pages)
+
+
+def mla_decode_multi_lowbit(fmt, q, cache, block_table, seq_lens, softmax_scale, max_seq_len=None, num_splits=0,
+                            out=None, lse=None, workspace=None, num_pages=None, stream=None):
+    """Multi-token decode: q [B, s_q, H, 576] are the queries of the last s_q tokens of every
+    sequence (already in the cache); query i sees tokens [0, L - s_q + 1 + i).  Returns
+    (out bf16 [B, s_q, H, 512], lse fp32 [B, s_q, H] or None)."""
+    import torch
+    B, s_q, H, MP, NP = _multi_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
+    if max_seq_len is None:
+        max_seq_len = MP * 64
+    S = int(num_splits)
+    if out is None:
+        out = torch.empty((B, s_q, H, 512), dtype=torch.bfloat16, device=q.device)
+    if workspace is None and S != 1:
+        workspace = torch.empty(mla_decode_workspace_bytes(fmt, B, s_q * H, S), dtype=torch.uint8, device=q.device)
+    _check(load_library().mla_decode_multi_lowbit(
+        ctypes.byref(format_struct(fmt)), _dev(q, "q", torch.bfloat16), s_q, _dev(cache, "cache", torch.uint8), NP,
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
+        int(max_seq_len), float(softmax_scale), S,
+        _opt(workspace, "workspace", torch.uint8), workspace.numel() if workspace is not None else 0,
+        _dev(out, "out", torch.bfloat16), _opt(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse
+
+
+def mla_decode_multi_partial(fmt, q, cache, block_table, seq_lens, softmax_scale, num_splits, workspace,
+                             max_seq_len=None, num_pages=None, stream=None) -> None:
+    """First stage of mla_decode_multi_lowbit; complete with mla_decode_combine(fmt, B, s_q * H, ...)."""
+    import torch
+    B, s_q, H, MP, NP = _multi_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
+    if max_seq_len is None:
+        max_seq_len = MP * 64
+    _check(load_library().mla_decode_multi_partial(
+        ctypes.byref(format_struct(fmt)), _dev(q, "q", torch.bfloat16), s_q, _dev(cache, "cache", torch.uint8), NP,
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
         int(max_seq_len), float(softmax_scale), int(num_splits), _dev(workspace, "workspace", torch.uint8),
         workspace.numel(), _stream(stream)))
 

@@ -89,7 +89,11 @@ struct DecodeShape {
   int fmt;
   int splits;
   int pages_per_split;
+  int s_q = 1;  // query tokens per sequence
 };
+
+// Query tokens per sequence accepted by the multi-token entry points.
+constexpr int kMaxQueries = 16;
 
 mla_status_t check_decode(const mla_format_t* fmt, const void* q, const void* cache, int64_t num_pages,
                           const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
@@ -136,16 +140,20 @@ mla::DecodeArgs make_args(const void* q, const void* cache, int64_t num_pages, c
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.batch = batch;
-  a.heads = num_heads;
+  a.heads = sh.s_q * num_heads;  // rows per sequence
+  a.s_q = sh.s_q;
+  a.qheads = num_heads;
+  a.chunk_heads = num_heads < 128 / sh.s_q ? num_heads : 128 / sh.s_q;
   a.max_pages = max_pages_per_seq;
   a.num_splits = sh.splits;
   a.pages_per_split = sh.pages_per_split;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   if (workspace) {
+    const int rows = sh.s_q * num_heads;
     a.o_part = (float*)workspace;
-    a.lse_part = (float*)((char*)workspace + partial_o_bytes(batch, num_heads, sh.splits));
-    a.meta = (int*)((char*)workspace + partial_o_bytes(batch, num_heads, sh.splits) +
-                    partial_lse_bytes(batch, num_heads, sh.splits));
+    a.lse_part = (float*)((char*)workspace + partial_o_bytes(batch, rows, sh.splits));
+    a.meta = (int*)((char*)workspace + partial_o_bytes(batch, rows, sh.splits) +
+                    partial_lse_bytes(batch, rows, sh.splits));
   }
   return a;
 }
@@ -163,20 +171,24 @@ void set_append(mla::DecodeArgs& a, const Append& ap) {
   a.append_cache = (uint8_t*)ap.cache;
 }
 
-mla_status_t decode_partial(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,
-                            const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
-                            int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale, int32_t num_splits,
-                            void* workspace, size_t ws_bytes, const Append& ap, void* stream) {
+mla_status_t decode_partial(const mla_format_t* fmt, const void* q_bf16, int32_t s_q, const void* cache,
+                            int64_t num_pages, const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                            int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale,
+                            int32_t num_splits, void* workspace, size_t ws_bytes, const Append& ap, void* stream) {
   DecodeShape sh;
   mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
                                  max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
   if (st != MLA_OK) return st;
+  if (s_q < 1 || s_q > kMaxQueries)
+    return fail(MLA_ERR_INVALID_ARG, "num_queries must be in 1..%d (got %d)", kMaxQueries, s_q);
+  sh.s_q = s_q;
   if (batch == 0) return MLA_OK;
+  const int rows = s_q * num_heads;
   if (!workspace || !aligned(workspace, 256))
     return fail(MLA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
-  if (ws_bytes < workspace_bytes(batch, num_heads, sh.splits))
+  if (ws_bytes < workspace_bytes(batch, rows, sh.splits))
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
-                workspace_bytes(batch, num_heads, sh.splits));
+                workspace_bytes(batch, rows, sh.splits));
   mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
                                 max_pages_per_seq, softmax_scale, sh, workspace);
   set_append(a, ap);
@@ -190,7 +202,9 @@ mla_status_t decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_
                             const void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out, void* stream) {
   if (format_id(fmt) < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
   if (batch < 0 || batch > 65535) return fail(MLA_ERR_INVALID_ARG, "batch must be in 0..65535");
-  if (num_heads < 1 || num_heads > 128) return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..128");
+  if (num_heads < 1 || num_heads > 128 * kMaxQueries)
+    return fail(MLA_ERR_UNSUPPORTED, "rows per sequence (num_heads, times num_queries) must be in 1..%d",
+                128 * kMaxQueries);
   if (num_splits < 0 || num_splits > kMaxSplits) return fail(MLA_ERR_INVALID_ARG, "num_splits must be in 0..64");
   if (batch == 0) return MLA_OK;
   if (!workspace || !out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
@@ -211,15 +225,18 @@ mla_status_t decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_
   return MLA_OK;
 }
 
-mla_status_t decode_full(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,
-                         const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t num_heads,
-                         int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale, int32_t num_splits,
-                         void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out, const Append& ap,
-                         void* stream) {
+mla_status_t decode_full(const mla_format_t* fmt, const void* q_bf16, int32_t s_q, const void* cache,
+                         int64_t num_pages, const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                         int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale,
+                         int32_t num_splits, void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out,
+                         const Append& ap, void* stream) {
   DecodeShape sh;
   mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
                                  max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
   if (st != MLA_OK) return st;
+  if (s_q < 1 || s_q > kMaxQueries)
+    return fail(MLA_ERR_INVALID_ARG, "num_queries must be in 1..%d (got %d)", kMaxQueries, s_q);
+  sh.s_q = s_q;
   if (batch == 0) return MLA_OK;
   if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MLA_ERR_INVALID_ARG, "out must be a 16-byte aligned pointer");
   if (lse_out && !aligned(lse_out, 4)) return fail(MLA_ERR_INVALID_ARG, "lse_out must be 4-byte aligned");
@@ -233,10 +250,10 @@ mla_status_t decode_full(const mla_format_t* fmt, const void* q_bf16, const void
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return MLA_OK;
   }
-  st = decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
-                      max_seq_len, softmax_scale, sh.splits, workspace, ws_bytes, ap, stream);
+  st = decode_partial(fmt, q_bf16, s_q, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                      max_pages_per_seq, max_seq_len, softmax_scale, sh.splits, workspace, ws_bytes, ap, stream);
   if (st != MLA_OK) return st;
-  return decode_combine(fmt, batch, num_heads, sh.splits, workspace, ws_bytes, out_bf16, lse_out, stream);
+  return decode_combine(fmt, batch, s_q * num_heads, sh.splits, workspace, ws_bytes, out_bf16, lse_out, stream);
 }
 
 }  // namespace
@@ -283,7 +300,7 @@ mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16, con
                                 int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
                                 float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
                                 void* stream) {
-  return decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+  return decode_partial(fmt, q_bf16, 1, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
                         max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, Append{}, stream);
 }
 
@@ -298,7 +315,7 @@ mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16, cons
                                int32_t num_heads, int32_t max_pages_per_seq, int32_t max_seq_len,
                                float softmax_scale, int32_t num_splits, void* workspace, size_t ws_bytes,
                                void* out_bf16, float* lse_out, void* stream) {
-  return decode_full(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+  return decode_full(fmt, q_bf16, 1, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
                      max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, out_bf16, lse_out, Append{}, stream);
 }
 
@@ -317,7 +334,7 @@ mla_status_t mla_decode_append_partial(const mla_format_t* fmt, const void* late
   ap.latent = latent_new_bf16;
   ap.rope = rope_new_bf16;
   ap.cache = cache;
-  return decode_partial(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+  return decode_partial(fmt, q_bf16, 1, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
                         max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, ap, stream);
 }
 
@@ -336,8 +353,29 @@ mla_status_t mla_decode_append_lowbit(const mla_format_t* fmt, const void* laten
   ap.latent = latent_new_bf16;
   ap.rope = rope_new_bf16;
   ap.cache = cache;
-  return decode_full(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+  return decode_full(fmt, q_bf16, 1, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
                      max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, out_bf16, lse_out, ap, stream);
+}
+
+mla_status_t mla_decode_multi_lowbit(const mla_format_t* fmt, const void* q_bf16, int32_t num_queries,
+                                     const void* cache, int64_t num_pages, const int32_t* block_table,
+                                     const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                     int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale,
+                                     int32_t num_splits, void* workspace, size_t ws_bytes, void* out_bf16,
+                                     float* lse_out, void* stream) {
+  return decode_full(fmt, q_bf16, num_queries, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                     max_pages_per_seq, max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, out_bf16, lse_out,
+                     Append{}, stream);
+}
+
+mla_status_t mla_decode_multi_partial(const mla_format_t* fmt, const void* q_bf16, int32_t num_queries,
+                                      const void* cache, int64_t num_pages, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t batch, int32_t num_heads,
+                                      int32_t max_pages_per_seq, int32_t max_seq_len, float softmax_scale,
+                                      int32_t num_splits, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_partial(fmt, q_bf16, num_queries, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                        max_pages_per_seq, max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, Append{},
+                        stream);
 }
 
 }  // extern "C"

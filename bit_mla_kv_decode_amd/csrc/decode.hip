@@ -338,10 +338,36 @@ struct SplitAcc {
 constexpr float kRefLift = 40.0f;
 constexpr float kMaxLift = 80.0f;
 
+// Rows.  With s_q query tokens per sequence and H heads, the rows of sequence
+// b are (query i, head h) -> i H + h, which is how q, the outputs and the
+// partial rows are laid out.  Head chunk c of a launch covers heads
+// [c Hc, c Hc + Hc) of every query: workgroup row r -> (r / Hc, c Hc + r % Hc).
+// Query i sees tokens [0, L - (s_q - 1) + i) (the query tokens are the last
+// s_q of the sequence, each seeing itself and the ones before it).
+struct RowOf {
+  int g;      // row of the sequence
+  int limit;  // tokens visible to it
+  bool valid;
+};
+
+__device__ __forceinline__ RowOf row_of(const DecodeArgs& a, int chunk, int L, int r) {
+  const int i = r / a.chunk_heads, h = chunk * a.chunk_heads + r % a.chunk_heads;
+  RowOf o;
+  o.valid = i < a.s_q && h < a.qheads;
+  o.g = i * a.qheads + h;
+  o.limit = L - (a.s_q - 1) + i;
+  return o;
+}
+
+// A reference that stays finite when a row sees no token of the piece (its
+// logits are all -inf): the weights are then exactly 0.
+__device__ __forceinline__ float finite_ref(float m) { return fmaxf(m, -3.0e38f); }
+
 template <int F>
 __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int k0,
-                                           int k1, const bf16x8 (&qr)[kQRegSteps], bool fixed, float m_fixed,
-                                           SplitAcc& acc) {
+                                           int k1, const bf16x8 (&qr)[kQRegSteps], int limit, bool fixed,
+                                           float m_fixed, SplitAcc& acc) {
+  const int limit_min = L - (a.s_q - 1);  // the smallest row limit (uniform)
   const int lane = threadIdx.x & 63, hi = lane >> 5;
   const __bf16* qrow = smem + 2 * kTile + ((threadIdx.x >> 6) * 32 + (lane & 31)) * kQRow + 8 * hi;
   // transposing-read addresses for the P.V operand: lane (g, i) = (lane / 16,
@@ -356,7 +382,7 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
 #pragma unroll
   for (int ct = 0; ct < 16; ++ct) acc.o[ct] = (f32x16){};
   acc.l_sum = 0.0f;
-  acc.m_ref = fixed ? m_fixed : -INFINITY;
+  acc.m_ref = fixed ? finite_ref(m_fixed) : -INFINITY;
   acc.m_seen = -INFINITY;
   bool lifted = false;
 
@@ -375,7 +401,6 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
     const int kn = min(k + 1, k1 - 1);
     fill.load(a.cache, win.page_of(kn), kn & 1, a.num_pages);
 
-    const int nvalid = min(kTileTok, L - k * kTileTok);
     // ---- S^T = khat . q^T for the 32 tokens of the tile.  Operands are read
     //      4 k-steps ahead; scheduling barriers pin that order so LDS latency
     //      hides behind the MFMAs instead of stalling each one.
@@ -397,16 +422,17 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- softmax weights (log2 domain); reg r is token 8 (r / 4) + 4 hi + r % 4
-    if (nvalid < kTileTok) {  // only the sequence's last tile is partial
+    if ((k + 1) * kTileTok > limit_min) {  // the last tokens: the row's limit (and the sequence end)
+      const int lt = limit - k * kTileTok;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[r] = -INFINITY;
+        if (8 * (r >> 2) + 4 * hi + (r & 3) >= lt) s[r] = -INFINITY;
     }
     if (k == k0 && !fixed) {  // a pass's reference: the first tile's max (uniform branch)
       float smax = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
-      acc.m_ref = fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift;
+      acc.m_ref = finite_ref(fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift);
     }
     // the weights need only the fixed reference, not this tile's max.  Regs
     // r < 8 are the tokens of P.V k-step 0 (tokens 0..15): those weights come
@@ -526,8 +552,9 @@ constexpr int kXchFloats = 64 * 16;  // one wavefront's partial S^T block
 
 template <int F, int C, int D>
 __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int k0,
-                                              int k1, const bf16x8 (&qr)[36 / C], bool fixed, float m_fixed,
-                                              CsAcc<C>& acc) {
+                                              int k1, const bf16x8 (&qr)[36 / C], int limit, bool fixed,
+                                              float m_fixed, CsAcc<C>& acc) {
+  const int limit_min = L - (a.s_q - 1);
   constexpr int NK = 36 / C, NCT = 16 / C;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5;
   const int part = wave % C, group = wave / C;
@@ -540,7 +567,7 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
 #pragma unroll
   for (int i = 0; i < NCT; ++i) acc.o[i] = (f32x16){};
   acc.l_sum = 0.0f;
-  acc.m_ref = fixed ? m_fixed : -INFINITY;
+  acc.m_ref = fixed ? finite_ref(m_fixed) : -INFINITY;
   acc.m_seen = -INFINITY;
   bool lifted = false;
 
@@ -567,7 +594,6 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       if (k >= k1) break;  // uniform
       __bf16* tile = smem + ((k - k0) & 1) * kTile;
       __bf16* next = smem + ((k - k0 + 1) & 1) * kTile;
-      const int nvalid = min(kTileTok, L - k * kTileTok);
       // ---- partial S^T over this part's k-steps, operands read 4 ahead
       f32x16 s = {};
       const __bf16* arow = tile + rho(lane & 31) * kRow + 8 * hi + 16 * (part * NK);
@@ -601,16 +627,17 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
         }
       }
       // ---- softmax weights, as in split_pass
-      if (nvalid < kTileTok) {
+      if ((k + 1) * kTileTok > limit_min) {
+        const int lt = limit - k * kTileTok;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[r] = -INFINITY;
+          if (8 * (r >> 2) + 4 * hi + (r & 3) >= lt) s[r] = -INFINITY;
       }
       if (k == k0 && !fixed) {
         float smax = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
-        acc.m_ref = fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift;
+        acc.m_ref = finite_ref(fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift);
       }
       const float neg_ref = -acc.m_ref;
       float ps = 0.0f;
@@ -686,16 +713,18 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
 }
 
 template <bool kDirect, int C>
-__device__ __forceinline__ void write_split_cs(const DecodeArgs& a, int b, int64_t slot, int head, const CsAcc<C>& acc) {
+__device__ __forceinline__ void write_split_cs(const DecodeArgs& a, int b, int64_t slot, const RowOf& row,
+                                               const CsAcc<C>& acc) {
   constexpr int NCT = 16 / C;
   const int hi = (threadIdx.x & 63) >> 5, part = (threadIdx.x >> 6) % C;
   const float l_tot = acc.l_sum + wave_partner(acc.l_sum);
-  const float inv = 1.0f / l_tot;
-  const float lse = (acc.m_ref + __log2f(l_tot)) * 0.69314718055994531f;
-  const int H = a.heads;
-  if (head >= H) return;
+  // a row that sees no token of the piece: output 0, lse -inf
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse = l_tot > 0.0f ? (acc.m_ref + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  const int R = a.heads, head = row.g;
+  if (!row.valid) return;
   if (kDirect) {
-    __bf16* orow = a.out + ((int64_t)b * H + head) * kDc + 4 * hi + 32 * (part * NCT);
+    __bf16* orow = a.out + ((int64_t)b * R + head) * kDc + 4 * hi + 32 * (part * NCT);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -704,10 +733,10 @@ __device__ __forceinline__ void write_split_cs(const DecodeArgs& a, int b, int64
         const unsigned w1 = pack_bf16x2(acc.o[ct][4 * rq + 2] * inv, acc.o[ct][4 * rq + 3] * inv);
         *(uint2*)(orow + 32 * ct + 8 * rq) = make_uint2(w0, w1);
       }
-    if (a.lse_out && hi == 0 && part == 0) a.lse_out[b * H + head] = lse;
+    if (a.lse_out && hi == 0 && part == 0) a.lse_out[b * R + head] = lse;
   } else {
-    const int64_t row = slot * H + head;
-    float* orow = a.o_part + row * kDc + 4 * hi + 32 * (part * NCT);
+    const int64_t prow = slot * R + head;
+    float* orow = a.o_part + prow * kDc + 4 * hi + 32 * (part * NCT);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -716,22 +745,24 @@ __device__ __forceinline__ void write_split_cs(const DecodeArgs& a, int b, int64
                          acc.o[ct][4 * rq + 3] * inv};
         *(f32x4*)(orow + 32 * ct + 8 * rq) = v;
       }
-    if (hi == 0 && part == 0) a.lse_part[row] = lse;
+    if (hi == 0 && part == 0) a.lse_part[prow] = lse;
   }
 }
 
 // Writes one pass result: the final bf16 output (direct mode) or an fp32
-// partial row at a.o_part[row * 512] / a.lse_part[row] (row = slot * H + head).
+// partial row at a.o_part[prow * 512] / a.lse_part[prow] (prow = slot * R + row).
 template <bool kDirect>
-__device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t slot, int head, const SplitAcc& acc) {
+__device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t slot, const RowOf& row,
+                                            const SplitAcc& acc) {
   const int hi = (threadIdx.x & 63) >> 5;
   const float l_tot = acc.l_sum + wave_partner(acc.l_sum);
-  const float inv = 1.0f / l_tot;
-  const float lse = (acc.m_ref + __log2f(l_tot)) * 0.69314718055994531f;
-  const int H = a.heads;
-  if (head >= H) return;
+  // a row that sees no token of the piece: output 0, lse -inf
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse = l_tot > 0.0f ? (acc.m_ref + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  const int R = a.heads, head = row.g;
+  if (!row.valid) return;
   if (kDirect) {
-    __bf16* orow = a.out + ((int64_t)b * H + head) * kDc + 4 * hi;
+    __bf16* orow = a.out + ((int64_t)b * R + head) * kDc + 4 * hi;
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
@@ -740,10 +771,10 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t 
         const unsigned w1 = pack_bf16x2(acc.o[ct][4 * rq + 2] * inv, acc.o[ct][4 * rq + 3] * inv);
         *(uint2*)(orow + 32 * ct + 8 * rq) = make_uint2(w0, w1);
       }
-    if (a.lse_out && hi == 0) a.lse_out[b * H + head] = lse;
+    if (a.lse_out && hi == 0) a.lse_out[b * R + head] = lse;
   } else {
-    const int64_t row = slot * H + head;
-    float* orow = a.o_part + row * kDc + 4 * hi;
+    const int64_t prow = slot * R + head;
+    float* orow = a.o_part + prow * kDc + 4 * hi;
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
@@ -752,17 +783,19 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t 
                          acc.o[ct][4 * rq + 3] * inv};
         *(f32x4*)(orow + 32 * ct + 8 * rq) = v;
       }
-    if (hi == 0) a.lse_part[row] = lse;
+    if (hi == 0) a.lse_part[prow] = lse;
   }
 }
 
-// Attention of sequence b over its tiles [k0, k1) (non-empty), written to
-// `slot`.  Called by every thread of the workgroup (uniform control flow).
+// Attention of sequence b over its tiles [k0, k1) (non-empty) for the rows of
+// head chunk `chunk`, written to `slot`.  Called by every thread of the
+// workgroup (uniform control flow).
 template <int F, bool kDirect, int C>
 __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem, int b, int L, int k0, int k1,
-                                              int64_t slot) {
+                                              int64_t slot, int chunk) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int H = a.heads;
+  const int R = a.heads;                   // rows of the sequence
+  const int rows = a.s_q * a.chunk_heads;  // rows of this workgroup
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
   // fused append: the piece holding the sequence's last tile writes the new
@@ -777,49 +810,51 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem,
   }
   __syncthreads();  // the previous range (if any) has finished with LDS
   if constexpr (C > 1) {
-    // channel split: every wavefront has heads (the launcher picks C from H)
+    // channel split: every wavefront has rows (the launcher picks C from the row count)
     constexpr int NK = 36 / C;
     const int part = wave % C, group = wave / C;
-    const int head = group * 32 + (lane & 31), hi = lane >> 5;
+    const RowOf row = row_of(a, chunk, L, group * 32 + (lane & 31));
+    const int hi = lane >> 5;
     bf16x8 qr[NK];
     {
-      const int hq = head < H ? head : H - 1;
-      const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi + 16 * (part * NK);
+      const __bf16* qh = a.q + ((int64_t)b * R + (row.valid ? row.g : 0)) * kD + 8 * hi + 16 * (part * NK);
       const bf16x8 zero = {};
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
         const bf16x8 v = *(const bf16x8*)(qh + 16 * i);
-        qr[i] = head < H ? v : zero;
+        qr[i] = row.valid ? v : zero;
       }
     }
     bool fixed = false;
     float m_fixed = 0.0f;
     for (int pass = 0;; ++pass) {
       CsAcc<C> acc;
-      const bool lifted = split_pass_cs<F, C, 3>(a, smem, bt, L, k0, k1, qr, fixed, m_fixed, acc);
+      const bool lifted = split_pass_cs<F, C, 3>(a, smem, bt, L, k0, k1, qr, row.limit, fixed, m_fixed, acc);
       const bool redo = __syncthreads_or(lifted);
       if (!redo || pass > 0) {
-        write_split_cs<kDirect, C>(a, b, slot, head, acc);
+        write_split_cs<kDirect, C>(a, b, slot, row, acc);
         return;
       }
       fixed = true;
       m_fixed = acc.m_seen;
     }
   } else {
-    // stage the LDS k-steps of q (zeros for heads >= H): LDS chunk c of head h
-    // holds channels 16 (2 (c / 2)) + 8 (c % 2) + [0, 8); the first tile's
-    // barrier publishes it
+    // stage the LDS k-steps of q (zeros for rows without a head): LDS chunk c
+    // of row r holds channels 16 (2 (c / 2)) + 8 (c % 2) + [0, 8); the first
+    // tile's barrier publishes it
     {
       __bf16* ql = smem + 2 * kTile;
       for (int ci = tid; ci < 128 * (kQLds / 8); ci += kThreads) {
-        const int h = ci / (kQLds / 8), c = ci % (kQLds / 8);
+        const int r = ci / (kQLds / 8), c = ci % (kQLds / 8);
+        const RowOf qrow = row_of(a, chunk, L, r);
         bf16x8 v = {};
-        if (h < H) v = *(const bf16x8*)(a.q + ((int64_t)b * H + h) * kD + 32 * (c >> 1) + 8 * (c & 1));
-        *(bf16x8*)(ql + h * kQRow + 8 * c) = v;
+        if (r < rows && qrow.valid)
+          v = *(const bf16x8*)(a.q + ((int64_t)b * R + qrow.g) * kD + 32 * (c >> 1) + 8 * (c & 1));
+        *(bf16x8*)(ql + r * kQRow + 8 * c) = v;
       }
     }
 
-    if (wave * 32 >= H) {  // no heads for this wavefront: fill only (uniform per wave)
+    if (wave * 32 >= rows) {  // no rows for this wavefront: fill only (uniform per wave)
       for (int pass = 0;; ++pass) {
         split_pass_fill_only<F>(a, smem, bt, L, k0, k1);
         const bool redo = __syncthreads_or(0);
@@ -827,20 +862,19 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem,
       }
     }
 
-    const int head = wave * 32 + (lane & 31);
+    const RowOf row = row_of(a, chunk, L, wave * 32 + (lane & 31));
     const int hi = lane >> 5;
-    // q^T operand: lane holds head `head`, channels 16 ks + 8 hi + [0, 8) of the
+    // q^T operand: lane holds row `row`, channels 16 ks + 8 hi + [0, 8) of the
     // register k-steps (odd ks < 32, and 32..35); the even ks < 32 are in LDS
     bf16x8 qr[kQRegSteps];
     {
-      const int hq = head < H ? head : H - 1;
-      const __bf16* qh = a.q + ((int64_t)b * H + hq) * kD + 8 * hi;
+      const __bf16* qh = a.q + ((int64_t)b * R + (row.valid ? row.g : 0)) * kD + 8 * hi;
       const bf16x8 zero = {};
 #pragma unroll
       for (int ks = 0; ks < 36; ++ks) {
         if (q_in_lds(ks)) continue;
         const bf16x8 v = *(const bf16x8*)(qh + 16 * ks);
-        qr[q_reg_index(ks)] = head < H ? v : zero;
+        qr[q_reg_index(ks)] = row.valid ? v : zero;
       }
     }
     // pass 0 takes the first tile's max (plus kRefLift) as reference; a second
@@ -850,10 +884,10 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem,
     float m_fixed = 0.0f;
     for (int pass = 0;; ++pass) {
       SplitAcc acc;
-      const bool lifted = split_pass<F>(a, smem, bt, L, k0, k1, qr, fixed, m_fixed, acc);
+      const bool lifted = split_pass<F>(a, smem, bt, L, k0, k1, qr, row.limit, fixed, m_fixed, acc);
       const bool redo = __syncthreads_or(lifted);
       if (!redo || pass > 0) {
-        write_split<kDirect>(a, b, slot, head, acc);
+        write_split<kDirect>(a, b, slot, row, acc);
         return;
       }
       fixed = true;
@@ -872,25 +906,30 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
 template <int F, bool kDirect, int C>
 __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
-  const int split = blockIdx.x, b = blockIdx.y;
+  const int split = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
   const int tid = threadIdx.x;
-  const int H = a.heads;
+  const int R = a.heads;
   const int L = clamped_len(a, b);
   const int n_pages = (L + kPage - 1) / kPage;
   const int p0 = split * a.pages_per_split;
   const int p1 = (split == a.num_splits - 1) ? n_pages : min(p0 + a.pages_per_split, n_pages);
-  if (p0 >= p1) {  // empty split
-    if (kDirect) {
-      for (int i = tid; i < H * kDc; i += kThreads) a.out[(int64_t)b * H * kDc + i] = (__bf16)0.0f;
-      if (a.lse_out && tid < H) a.lse_out[b * H + tid] = -INFINITY;
-    } else if (tid < H) {
-      a.lse_part[((int64_t)b * a.num_splits + split) * H + tid] = -INFINITY;
+  if (p0 >= p1) {  // empty split: the chunk's rows get weight 0 (direct mode: output 0, lse -inf)
+    const int rows = a.s_q * a.chunk_heads;
+    for (int i = tid; i < rows * (kDirect ? kDc / 8 : 1); i += kThreads) {
+      const RowOf row = row_of(a, chunk, L, kDirect ? i / (kDc / 8) : i);
+      if (!row.valid) continue;
+      if (kDirect) {
+        *(u32x4*)(a.out + ((int64_t)b * R + row.g) * kDc + 8 * (i % (kDc / 8))) = (u32x4){0u, 0u, 0u, 0u};
+        if (a.lse_out && i % (kDc / 8) == 0) a.lse_out[b * R + row.g] = -INFINITY;
+      } else {
+        a.lse_part[((int64_t)b * a.num_splits + split) * R + row.g] = -INFINITY;
+      }
     }
     return;
   }
   // tiles are half pages: tile k covers tokens [32 k, 32 k + 32)
   process_range<F, kDirect, C>(a, smem, b, L, 2 * p0, min(2 * p1, (L + kTileTok - 1) / kTileTok),
-                            (int64_t)b * a.num_splits + split);
+                               (int64_t)b * a.num_splits + split, chunk);
 }
 
 // Balanced partition: the batch's pages, laid end to end in sequence order
@@ -973,7 +1012,7 @@ __device__ __forceinline__ void flat_next_piece(const DecodeArgs& a, FlatWalk& w
     const int64_t lo = off > start ? off : start;
     const int64_t hi = off + n < end ? off + n : end;
     const bool seg = b < a.batch && lo < hi;
-    if (seg && off >= start) {
+    if (seg && off >= start && blockIdx.y == 0) {
       // the first page of b is in this share: b's slots run from w + b to
       // wl + b, wl the share holding b's last page
       const int64_t x = off + n - 1;
@@ -1015,8 +1054,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_flat(const DecodeArgs a)
   }
   __syncthreads();
   const int64_t T = (int64_t)uniform64(s_total);
-  // empty sequences own no slots: record (0, 0) for them (strided over workgroups)
-  for (int b = (int)w * kThreads + tid; b < a.batch; b += (int)gridDim.x * kThreads)
+  // empty sequences own no slots: record (0, 0) for them (strided over
+  // workgroups; head chunk 0 writes all slot records)
+  for (int b = (int)w * kThreads + tid; blockIdx.y == 0 && b < a.batch; b += (int)gridDim.x * kThreads)
     if (clamped_len(a, b) == 0) {
       a.meta[2 * b] = 0;
       a.meta[2 * b + 1] = 0;
@@ -1040,7 +1080,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_flat(const DecodeArgs a)
     const int L = __builtin_amdgcn_readfirstlane(walk.piece[1]);
     const int k0 = __builtin_amdgcn_readfirstlane(walk.piece[2]);
     const int k1 = __builtin_amdgcn_readfirstlane(walk.piece[3]);
-    process_range<F, false, C>(a, smem, b, L, k0, k1, w + b);
+    process_range<F, false, C>(a, smem, b, L, k0, k1, w + b, blockIdx.y);
   }
 }
 
@@ -1136,17 +1176,21 @@ static hipError_t set_lds(K kernel, bool& done) {  // benign race: the attribute
 // unquantized baseline always uses the latter).  Measured on 8 x 131072 C4R4
 // tokens: 16-32 heads 0.31 -> 0.26 ms; a 2-way split at 64 heads was slower
 // than one group per wavefront, so it is not used.
-static int channel_split(int fmt, int heads) {
+static int channel_split(int fmt, int rows) {
   if (fmt == kBF16) return 1;
-  return heads <= 32 ? 4 : 1;
+  return rows <= 32 ? 4 : 1;
 }
+
+// Head chunks of a launch (grid dimension): s_q * chunk_heads rows each.
+static int head_chunks(const DecodeArgs& a) { return (a.qheads + a.chunk_heads - 1) / a.chunk_heads; }
 
 template <int F, bool D, int C>
 static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
   static bool attr_done = false;
   hipError_t e = set_lds(k_decode<F, D, C>, attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch), dim3(kThreads), kDecodeLds, stream, a);
+  hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch, head_chunks(a)), dim3(kThreads), kDecodeLds,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -1155,7 +1199,7 @@ static hipError_t launch_flat_one(const DecodeArgs& a, int groups, hipStream_t s
   static bool attr_done = false;
   hipError_t e = set_lds(k_decode_flat<F, C>, attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups), dim3(kThreads), kDecodeLds, stream, a);
+  hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups, head_chunks(a)), dim3(kThreads), kDecodeLds, stream, a);
   return hipGetLastError();
 }
 
@@ -1165,7 +1209,7 @@ static hipError_t launch_split(bool direct, const DecodeArgs& a, int batch, hipS
 }
 
 hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream) {
-  const int c = channel_split(fmt, a.heads);
+  const int c = channel_split(fmt, a.s_q * a.chunk_heads);
   if (fmt == kC4R4)
     return c == 4 ? launch_split<kC4R4, 4>(direct, a, batch, stream) : launch_split<kC4R4, 1>(direct, a, batch, stream);
   if (fmt == kC2R4)
@@ -1174,7 +1218,7 @@ hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, h
 }
 
 hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream) {
-  const int c = channel_split(fmt, a.heads);
+  const int c = channel_split(fmt, a.s_q * a.chunk_heads);
   if (fmt == kC4R4)
     return c == 4 ? launch_flat_one<kC4R4, 4>(a, groups, stream) : launch_flat_one<kC4R4, 1>(a, groups, stream);
   if (fmt == kC2R4)

@@ -11,7 +11,10 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int batch;
-  int heads;
+  int heads;             // rows per sequence: s_q * qheads
+  int s_q;               // query tokens per sequence (causal among themselves)
+  int qheads;            // heads per query token
+  int chunk_heads;       // heads per workgroup row block (s_q * chunk_heads <= 128)
   int max_pages;
   int num_splits;
   int pages_per_split;

@@ -11,6 +11,8 @@
       - bf16:    the unquantized-cache kernel on the C2R4 workload's data
       - heads:   head-count sweep at the 8 x 131072 C4R4 shape
       - pages:   contiguous vs randomly permuted page tables
+      - multi:   multi-token decode (s_q query tokens per sequence) on the
+                 8 x 131072 C4R4 cache: 16 heads x s_q 1..8, 128 heads x 2
   python -m bit_mla_kv_decode_amd.measure --counters
       the launches a rocprofv3 --pmc run counts: a 1 GiB plain copy three
       times, then the 8 x 131072 C4R4 decode (bench configuration: fused append +
@@ -216,8 +218,36 @@ def section_pages():
         torch.cuda.empty_cache()
 
 
+def section_multi():
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    from bit_mla_kv_decode_amd import workloads as W
+    w = W.WORKLOADS["c4r4_128k"]
+    log("multi-token decode on %s" % w.name)
+    c = Case(w)
+    B = w.batch
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for H, s_q in ((16, 1), (16, 2), (16, 4), (16, 8), (32, 4), (128, 1), (128, 2)):
+        q = torch.randn(B, s_q, H, 576, device="cuda", generator=g).to(torch.bfloat16)
+        ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, s_q * H, 0), dtype=torch.uint8, device="cuda")
+        R = len(c.caches)
+        t = _events(lambda i: mla.mla_decode_multi_partial(w.fmt, q, c.caches[i % R], c.btd, c.sld, w.softmax_scale,
+                                                           0, ws, max_seq_len=int(c.lens.max()), stream=st),
+                    20, 5, st)
+        tp = float(np.median(t))
+        tok = int(c.lens.sum())
+        fl = tok * flops_per_token(s_q * H)
+        emit({"row": "multi_token", "workload": w.name, "heads": H, "queries": s_q, "rows": s_q * H,
+              "decode_ms": round(tp, 4), "packed_GBps": round(c.packed / (tp * 1e-3) / 1e9, 1),
+              "TFLOPs": round(fl / (tp * 1e-3) / 1e12, 1),
+              "roofline_frac": round(max(c.packed / HBM_PEAK, fl / MFMA_BF16_PEAK) / (tp * 1e-3), 4)})
+    del c
+    torch.cuda.empty_cache()
+
+
 SECTIONS = {"peaks": section_peaks, "configs": section_configs, "bf16": section_bf16,
-            "heads": section_heads, "pages": section_pages}
+            "heads": section_heads, "pages": section_pages, "multi": section_multi}
 
 
 # ------------------------------------------------------------------ counters

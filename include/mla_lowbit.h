@@ -181,6 +181,38 @@ mla_status_t mla_decode_append_partial(const mla_format_t* fmt, const void* late
                                        float softmax_scale, int32_t num_splits, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* Multi-token decode (several query tokens per sequence, e.g. multi-token
+ * prediction or speculative decoding): the last num_queries tokens of every
+ * sequence are queries; query i (0 <= i < num_queries) sits at position
+ * seq_lens[b] - num_queries + i and attends to tokens [0, seq_lens[b] -
+ * num_queries + 1 + i), i.e. to itself and the tokens before it (their rows
+ * are already in the cache).  A query that sees no token gets output 0 and
+ * lse -inf.
+ *   q_bf16      [batch, num_queries, num_heads, d_c + d_r]
+ *   num_queries 1..16
+ *   out_bf16    [batch, num_queries, num_heads, d_c]
+ *   lse_out     [batch, num_queries, num_heads] fp32, or NULL
+ *   workspace   >= mla_decode_workspace_bytes(fmt, batch, num_queries * num_heads,
+ *               num_splits) bytes (the rows of a sequence are (query, head) pairs)
+ * Other arguments as mla_decode_lowbit.  With num_queries = 1 it is
+ * mla_decode_lowbit.  The cache is read once per group of up to 128 rows:
+ * num_queries * num_heads <= 128 reads it once. */
+mla_status_t mla_decode_multi_lowbit(const mla_format_t* fmt, const void* q_bf16, int32_t num_queries,
+                                     const void* cache, int64_t num_pages,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
+                                     int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                     void* workspace, size_t workspace_bytes, void* out_bf16,
+                                     float* lse_out, void* stream);
+/* First stage of mla_decode_multi_lowbit; complete it with
+ * mla_decode_combine(fmt, batch, num_queries * num_heads, num_splits, ...). */
+mla_status_t mla_decode_multi_partial(const mla_format_t* fmt, const void* q_bf16, int32_t num_queries,
+                                      const void* cache, int64_t num_pages,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
+                                      int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* The two stages of mla_decode_lowbit, for callers that schedule them
  * separately (for example to merge partial results computed elsewhere).
  * mla_decode_partial writes, for split s of sequence b, the normalized
@@ -202,6 +234,8 @@ mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16,
                                 int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
                                 int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                                 void* workspace, size_t workspace_bytes, void* stream);
+/* (mla_decode_combine's num_heads is the rows per sequence: num_heads, or
+ * num_queries * num_heads after mla_decode_multi_partial; at most 2048.) */
 mla_status_t mla_decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
                                 int32_t num_splits, const void* workspace, size_t workspace_bytes,
                                 void* out_bf16, float* lse_out, void* stream);

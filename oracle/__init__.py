@@ -189,6 +189,27 @@ def decode(fmt, q, cache, num_pages, block_table, seq_lens, softmax_scale,
     return out, lse
 
 
+def decode_multi(fmt, q, cache, num_pages, block_table, seq_lens, softmax_scale, nthreads=0):
+    """Multi-token decode: q [B, s_q, H, d_c + d_r] holds the queries of the
+    last s_q tokens of every sequence (already in the cache); query i sees
+    tokens [0, L - s_q + 1 + i) (itself and those before it, causal), none
+    when that count is <= 0 (output 0, lse -inf).  Each query is the
+    single-token decode of the sequence cut at its own position.
+
+    Returns (out [B, s_q, H, d_c], lse [B, s_q, H]) in float64."""
+    qq = _u16(q)
+    B, s_q, H, D = qq.shape
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    out = np.zeros((B, s_q, H, int(_fmt(fmt)[4])), dtype=np.float64)
+    lse = np.zeros((B, s_q, H), dtype=np.float64)
+    for i in range(s_q):
+        lens_i = np.maximum(sl - (s_q - 1) + i, 0).astype(np.int32)
+        o, l = decode(fmt, np.ascontiguousarray(qq[:, i]), cache, num_pages, block_table, lens_i, softmax_scale,
+                      nthreads=nthreads)
+        out[:, i], lse[:, i] = o, l
+    return out, lse
+
+
 def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
     """Merge partials o_parts [S, rows..., d] / lse_parts [S, rows...] (float64)."""
     o = np.ascontiguousarray(o_parts, dtype=np.float64)

@@ -164,3 +164,18 @@ def test_fused_append_argument_errors():
     assert call(batch=0, lat=None, rope=None) == mla.MLA_OK
     assert L.mla_decode_append_partial(_fmt(), None, A3, A, A, 10, A, A, 2, 128, 4, 256, 0.07, 0, A2, 1 << 30,
                                        None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_multi_token_argument_errors():
+    L = mla.load_library()
+
+    def call(nq=2, heads=64, splits=0, ws_bytes=1 << 30):
+        return L.mla_decode_multi_lowbit(_fmt(), A, nq, A, 10, A, A, 2, heads, 4, 256, 0.07, splits, A2, ws_bytes,
+                                         A, None, None)
+    assert call(nq=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(nq=17) == mla.MLA_ERR_INVALID_ARG
+    assert call(heads=129) == mla.MLA_ERR_UNSUPPORTED
+    need = mla.mla_decode_workspace_bytes("C4R4", 2, 2 * 64, 0)
+    assert call(ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
+    # the combine takes rows = num_queries * num_heads (up to 2048)
+    assert L.mla_decode_combine(_fmt(), 2, 2049, 0, A2, 1 << 40, A, None, None) == mla.MLA_ERR_UNSUPPORTED

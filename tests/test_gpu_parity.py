@@ -374,3 +374,39 @@ def test_fused_append_decode_equals_separate(fmt, splits, heads):
     ref, ref_lse = oracle.decode(OFMT[fmt], q, h2, npages, bt, lens, SCALE)
     assert_close(o2.float().cpu().numpy(), ref, "fused %s" % fmt)
     assert_lse(l2.cpu().numpy(), ref_lse)
+
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "BF16"])
+@pytest.mark.parametrize("s_q,heads", [(2, 64), (4, 8), (3, 100), (16, 16)])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_multi_token_decode(fmt, s_q, heads, splits):
+    """Several query tokens per sequence (causal among themselves): 128 rows in
+    one workgroup, 32 rows (channel split), and rows split into head chunks;
+    a sequence shorter than the query count; against oracle.decode_multi."""
+    _say("multi-token %s s_q=%d H=%d S=%d" % (fmt, s_q, heads, splits))
+    lens = [1500, 3, 70, 0, 64, 333]
+    w, lens, bt, npages, lat, rope, slots, _ = build(fmt, lens, heads, seed=s_q * 7 + heads, outliers=fmt == "C2R4")
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    g = torch.Generator().manual_seed(s_q + heads + splits)
+    q = torch.randn(len(lens), s_q, heads, 576, generator=g).to(torch.bfloat16)
+    lse = torch.empty(len(lens), s_q, heads, dtype=torch.float32, device="cuda")
+    out, _ = mla.mla_decode_multi_lowbit(fmt, q.cuda(), cache, torch.from_numpy(bt).cuda(),
+                                         torch.from_numpy(lens).cuda(), SCALE, max_seq_len=int(lens.max()),
+                                         num_splits=splits, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode_multi(OFMT[fmt], q, cache.cpu().numpy(), npages, bt, lens, SCALE)
+    assert_close(out.float().cpu().numpy(), ref, "multi %s s_q=%d H=%d" % (fmt, s_q, heads))
+    assert_lse(lse.cpu().numpy(), ref_lse)
+
+
+def test_multi_token_single_query_equals_decode():
+    fmt = "C4R4"
+    w, lens, bt, npages, lat, rope, slots, q = build(fmt, [900, 65, 1], 48, seed=77)
+    cache = gpu_cache(fmt, npages, lat, rope, slots)
+    btd, sld = torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+    for S in (0, 1, 4):
+        o1, _ = mla.mla_decode_lowbit(fmt, q.cuda(), cache, btd, sld, SCALE, num_splits=S)
+        o2, _ = mla.mla_decode_multi_lowbit(fmt, q.cuda()[:, None].contiguous(), cache, btd, sld, SCALE, num_splits=S)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2[:, 0])

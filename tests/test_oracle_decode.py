@@ -183,3 +183,36 @@ def test_decode_detects_page_errors():
     bad[0, 1] = npages + 5
     with pytest.raises(ValueError):
         oracle.decode(oracle.C4R4, q, cache, npages, bad, sl, SCALE)
+
+
+def test_multi_token_decode_is_causal_attention():
+    """decode_multi (queries of the last s_q tokens, each seeing itself and the
+    tokens before it) against PyTorch SDPA with an explicit causal mask on the
+    raw bf16 rows (the 16-bit path), with a sequence shorter than s_q."""
+    s_q, H = 3, 2
+    fmt = oracle.BF16
+    lens = [70, 2, 5]
+    cache, total, bt, lens_a, _, lat_all, rope_all = _build(fmt, lens, H=H, seed=21)
+    g = torch.Generator().manual_seed(22)
+    q = torch.randn(len(lens), s_q, H, 576, generator=g).to(torch.bfloat16)
+    out, lse = oracle.decode_multi(fmt, q, cache, total, bt, lens_a, SCALE)
+    for b, L in enumerate(lens):
+        k = torch.cat([lat_all[b], rope_all[b]], 1).double()
+        v = lat_all[b].double()
+        for i in range(s_q):
+            pos = L - s_q + i                     # position of query i; it sees tokens 0..pos
+            if pos < 0:
+                assert (out[b, i] == 0).all() and np.isneginf(lse[b, i]).all()
+                continue
+            mask = torch.arange(L) <= pos
+            qi = q[b, i].double()                 # [H, 576]
+            ref = F.scaled_dot_product_attention(qi[None], k[None], v[None], attn_mask=mask[None, None, :],
+                                                 scale=SCALE)[0]
+            logits = (qi @ k.T) * SCALE
+            ref_lse = torch.logsumexp(logits.masked_fill(~mask, float("-inf")), dim=-1)
+            assert np.allclose(out[b, i], ref.numpy(), rtol=1e-12, atol=1e-12)
+            assert np.allclose(lse[b, i], ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+    # one query is the single-token decode
+    o1, l1 = oracle.decode_multi(fmt, q[:, -1:], cache, total, bt, lens_a, SCALE)
+    o2, l2 = oracle.decode(fmt, q[:, -1], cache, total, bt, lens_a, SCALE)
+    assert np.array_equal(o1[:, 0], o2) and np.array_equal(l1[:, 0], l2)
