@@ -17,7 +17,7 @@ __all__ = [
     "mla_token_bytes", "mla_page_bytes", "mla_quant_append", "mla_decode_num_splits",
     "mla_decode_workspace_bytes", "mla_decode_lowbit", "mla_decode_partial", "mla_decode_combine",
     "mla_decode_append_lowbit", "mla_decode_append_partial", "mla_decode_multi_lowbit",
-    "mla_decode_multi_partial",
+    "mla_decode_multi_partial", "mla_absorb_q", "mla_project_out",
     "mla_last_error", "alloc_cache",
 ]
 
@@ -80,6 +80,8 @@ def load_library():
                                                    P, P, P]),
         "mla_decode_multi_partial": (ctypes.c_int, [FP, P, I32, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ,
                                                     P]),
+        "mla_absorb_q": (ctypes.c_int, [P, P, P, I32, I32, P, P]),
+        "mla_project_out": (ctypes.c_int, [P, P, I32, I32, P, P]),
         "mla_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -340,3 +342,30 @@ def balanced_workspace_views(fmt, workspace, batch, num_heads):
     l = workspace[o_bytes:o_bytes + slots * num_heads * 4].view(torch.float32).view(slots, num_heads)
     m = workspace[o_bytes + l_bytes:o_bytes + l_bytes + batch * 8].view(torch.int32).view(batch, 2)
     return o, l, m
+
+
+def mla_absorb_q(q_nope, q_pe, w_uk, q_out=None, stream=None):
+    """q [B, H, 576] = [per-head q_nope [B, H, 128] times w_uk [H, 512, 128] | q_pe [B, H, 64]] (bf16)."""
+    import torch
+    B, H, K = (int(v) for v in q_nope.shape)
+    if K != 128 or tuple(q_pe.shape) != (B, H, 64) or tuple(w_uk.shape) != (H, 512, 128):
+        raise ValueError("q_nope [B, H, 128], q_pe [B, H, 64], w_uk [H, 512, 128] expected")
+    if q_out is None:
+        q_out = torch.empty(B, H, 576, dtype=torch.bfloat16, device=q_nope.device)
+    _check(load_library().mla_absorb_q(_dev(q_nope, "q_nope", torch.bfloat16), _dev(q_pe, "q_pe", torch.bfloat16),
+                                       _dev(w_uk, "w_uk", torch.bfloat16), B, H,
+                                       _dev(q_out, "q_out", torch.bfloat16), _stream(stream)))
+    return q_out
+
+
+def mla_project_out(latent, w_uv, out=None, stream=None):
+    """o [B, H, 128] = per-head latent [B, H, 512] times w_uv [H, 128, 512] (bf16)."""
+    import torch
+    B, H, C = (int(v) for v in latent.shape)
+    if C != 512 or tuple(w_uv.shape) != (H, 128, 512):
+        raise ValueError("latent [B, H, 512] and w_uv [H, 128, 512] expected")
+    if out is None:
+        out = torch.empty(B, H, 128, dtype=torch.bfloat16, device=latent.device)
+    _check(load_library().mla_project_out(_dev(latent, "latent", torch.bfloat16), _dev(w_uv, "w_uv", torch.bfloat16),
+                                          B, H, _dev(out, "out", torch.bfloat16), _stream(stream)))
+    return out

@@ -378,4 +378,31 @@ mla_status_t mla_decode_multi_partial(const mla_format_t* fmt, const void* q_bf1
                         stream);
 }
 
+mla_status_t mla_absorb_q(const void* q_nope_bf16, const void* q_pe_bf16, const void* w_uk_bf16, int32_t batch,
+                          int32_t num_heads, void* q_out_bf16, void* stream) {
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  if (num_heads < 1 || num_heads > 1024) return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..1024");
+  if (batch == 0) return MLA_OK;
+  if (!q_nope_bf16 || !q_pe_bf16 || !w_uk_bf16 || !q_out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(q_nope_bf16, 16) || !aligned(w_uk_bf16, 16) || !aligned(q_out_bf16, 16) || !aligned(q_pe_bf16, 2))
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, w_uk and q_out must be 16-byte aligned");
+  hipError_t e = mla::launch_absorb_q(q_nope_bf16, q_pe_bf16, w_uk_bf16, batch, num_heads, q_out_bf16,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "absorb launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status_t mla_project_out(const void* latent_bf16, const void* w_uv_bf16, int32_t batch, int32_t num_heads,
+                             void* out_bf16, void* stream) {
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  if (num_heads < 1 || num_heads > 1024) return fail(MLA_ERR_UNSUPPORTED, "num_heads must be in 1..1024");
+  if (batch == 0) return MLA_OK;
+  if (!latent_bf16 || !w_uv_bf16 || !out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(latent_bf16, 16) || !aligned(w_uv_bf16, 16) || !aligned(out_bf16, 2))
+    return fail(MLA_ERR_INVALID_ARG, "latent and w_uv must be 16-byte aligned");
+  hipError_t e = mla::launch_project_out(latent_bf16, w_uv_bf16, batch, num_heads, out_bf16, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "projection launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
 }  // extern "C"

@@ -37,6 +37,11 @@ hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, h
 hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream);
 hipError_t launch_combine_flat(const float* o_part, const float* lse_part, const int* meta, int batch, int heads,
                                __bf16* out, float* lse_out, hipStream_t stream);
+// q [B, H, 576] = [q_nope W_UK^T | q_pe] per head; o [B, H, 128] = out W_UV^T per head
+hipError_t launch_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, int B, int H, void* q_out,
+                           hipStream_t stream);
+hipError_t launch_project_out(const void* latent, const void* w_uv, int B, int H, void* out, hipStream_t stream);
+
 hipError_t launch_combine(const float* o_part, const float* lse_part, int batch, int heads, int splits,
                           __bf16* out, float* lse_out, hipStream_t stream);
 

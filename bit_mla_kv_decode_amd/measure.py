@@ -13,6 +13,8 @@
       - pages:   contiguous vs randomly permuted page tables
       - multi:   multi-token decode (s_q query tokens per sequence) on the
                  8 x 131072 C4R4 cache: 16 heads x s_q 1..8, 128 heads x 2
+      - proj:    the absorbed projections (mla_absorb_q, mla_project_out) at
+                 128 heads, batch 8..128: weight GB/s
   python -m bit_mla_kv_decode_amd.measure --counters
       the launches a rocprofv3 --pmc run counts: a 1 GiB plain copy three
       times, then the 8 x 131072 C4R4 decode (bench configuration: fused append +
@@ -246,8 +248,34 @@ def section_multi():
     torch.cuda.empty_cache()
 
 
+def section_proj():
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    from bit_mla_kv_decode_amd import workloads as W
+    st = torch.cuda.current_stream()
+    H = 128
+    for B in (8, 32, 128):
+        q_nope, q_pe, w_uk, w_uv = (t.cuda() for t in W.absorb_inputs(B, H, seed=B))
+        # several weight copies so repeats read HBM, not the last-level cache
+        n = 24
+        wuks = [w_uk.clone() for _ in range(n)]
+        wuvs = [w_uv.clone() for _ in range(n)]
+        q = torch.empty(B, H, 576, dtype=torch.bfloat16, device="cuda")
+        lat = torch.randn(B, H, 512, device="cuda").to(torch.bfloat16)
+        o = torch.empty(B, H, 128, dtype=torch.bfloat16, device="cuda")
+        ta = float(np.median(_events(lambda i: mla.mla_absorb_q(q_nope, q_pe, wuks[i % n], q, stream=st), 20, 5, st)))
+        tp = float(np.median(_events(lambda i: mla.mla_project_out(lat, wuvs[i % n], o, stream=st), 20, 5, st)))
+        wbytes = H * 512 * 128 * 2
+        for name, t in (("absorb_q", ta), ("project_out", tp)):
+            emit({"row": "projection", "op": name, "batch": B, "heads": H, "ms": round(t, 4),
+                  "weight_GBps": round(wbytes / (t * 1e-3) / 1e9, 1),
+                  "TFLOPs": round(2.0 * B * H * 512 * 128 / (t * 1e-3) / 1e12, 2)})
+        del wuks, wuvs
+        torch.cuda.empty_cache()
+
+
 SECTIONS = {"peaks": section_peaks, "configs": section_configs, "bf16": section_bf16,
-            "heads": section_heads, "pages": section_pages, "multi": section_multi}
+            "heads": section_heads, "pages": section_pages, "multi": section_multi, "proj": section_proj}
 
 
 # ------------------------------------------------------------------ counters

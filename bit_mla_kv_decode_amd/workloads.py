@@ -180,3 +180,17 @@ def new_token_rows(w: Workload, lens: np.ndarray, device="cpu"):
         lat.append(l)
         rope.append(r)
     return torch.cat(lat, 0), torch.cat(rope, 0)
+
+
+def absorb_inputs(batch: int, heads: int, seed: int, device="cpu"):
+    """Synthetic weights and queries of the absorbed projections: q_nope
+    [B, H, 128] and q_pe [B, H, 64] ~ N(0, 1); w_uk [H, 512, 128] ~ N(0, 1/128)
+    and w_uv [H, 128, 512] ~ N(0, 1/512) (unit-variance outputs); bf16."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    def bf(a):
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(device)
+    q_nope = bf(g.standard_normal((batch, heads, 128)))
+    q_pe = bf(g.standard_normal((batch, heads, 64)))
+    w_uk = bf(g.standard_normal((heads, 512, 128)) / np.sqrt(128.0))
+    w_uv = bf(g.standard_normal((heads, 128, 512)) / np.sqrt(512.0))
+    return q_nope, q_pe, w_uk, w_uv

@@ -240,6 +240,27 @@ mla_status_t mla_decode_combine(const mla_format_t* fmt, int32_t batch, int32_t 
                                 int32_t num_splits, const void* workspace, size_t workspace_bytes,
                                 void* out_bf16, float* lse_out, void* stream);
 
+/* The absorbed projections around the decode (one MLA decode attention
+ * step).  The latent is the shared source of every head's key and value
+ * ("QuantMLA: INT4 (and INT2) for both halves of the MLA cache", TL;DR and
+ * flowchart): head h's key is W_UK[h] c and its value W_UV[h] c, so decode
+ * absorbs the query into latent space before attention and applies the value
+ * projection to its result after it.  fp32 accumulation, bf16
+ * round-to-nearest-even outputs; all pointers device, caller-owned.
+ *   mla_absorb_q:    q_out[b, h, 0:512]   = sum_k q_nope[b, h, k] w_uk[h, n, k]
+ *                    q_out[b, h, 512:576] = q_pe[b, h, :]
+ *     q_nope_bf16 [batch, num_heads, 128], q_pe_bf16 [batch, num_heads, 64],
+ *     w_uk_bf16 [num_heads, 512, 128] (n-major), q_out_bf16 [batch, num_heads, 576]
+ *     (the q of mla_decode_lowbit)
+ *   mla_project_out: out[b, h, j] = sum_c latent[b, h, c] w_uv[h, j, c]
+ *     latent_bf16 [batch, num_heads, 512] (the out of mla_decode_lowbit),
+ *     w_uv_bf16 [num_heads, 128, 512], out_bf16 [batch, num_heads, 128]
+ * num_heads 1..1024; q_nope, w_uk, q_out, latent, w_uv 16-byte aligned. */
+mla_status_t mla_absorb_q(const void* q_nope_bf16, const void* q_pe_bf16, const void* w_uk_bf16,
+                          int32_t batch, int32_t num_heads, void* q_out_bf16, void* stream);
+mla_status_t mla_project_out(const void* latent_bf16, const void* w_uv_bf16, int32_t batch,
+                             int32_t num_heads, void* out_bf16, void* stream);
+
 /* Description of the most recent non-OK status returned on this thread. */
 const char* mla_last_error(void);
 

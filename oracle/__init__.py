@@ -210,6 +210,31 @@ def decode_multi(fmt, q, cache, num_pages, block_table, seq_lens, softmax_scale,
     return out, lse
 
 
+def _f64(a) -> np.ndarray:
+    """bf16 tensor / uint16 bit patterns -> float64 values."""
+    u = _u16(a).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def absorb_q(q_nope, w_uk) -> np.ndarray:
+    """Absorbed query in latent space, per head (fp64): the latent is the
+    shared source of every head's key (QuantMLA pages: [P2] TL;DR and
+    flowchart), key_h = W_UK[h] c, so <q_nope, W_UK[h] c> = <W_UK[h]^T q_nope, c>.
+    q_nope [B, H, 128], w_uk [H, 512, 128] (n-major) -> [B, H, 512]."""
+    q = _f64(q_nope)
+    w = _f64(w_uk)
+    return np.einsum("bhk,hnk->bhn", q, w)
+
+
+def project_out(latent, w_uv) -> np.ndarray:
+    """Value projection applied after attention, per head (fp64): value_h =
+    W_UV[h] c, so sum_t p_t W_UV[h] c_t = W_UV[h] sum_t p_t c_t.
+    latent [B, H, 512] (bf16 or float64), w_uv [H, 128, 512] -> [B, H, 128]."""
+    x = latent if (isinstance(latent, np.ndarray) and latent.dtype == np.float64) else _f64(latent)
+    w = _f64(w_uv)
+    return np.einsum("bhc,hjc->bhj", x, w)
+
+
 def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
     """Merge partials o_parts [S, rows..., d] / lse_parts [S, rows...] (float64)."""
     o = np.ascontiguousarray(o_parts, dtype=np.float64)
