@@ -36,6 +36,8 @@
 //   5. per piece: O / l and lse = m + log l are written as fp32 partials (or,
 //      with one split, the final bf16 output directly).
 // A second kernel merges the pieces with log-sum-exp weights.
+#include <atomic>
+
 #include "append.h"
 #include "kernels.h"
 
@@ -512,8 +514,9 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
   return lifted;
 }
 
-// The same tile sequence for a wavefront that owns no heads (num_heads below
-// 32 w): it only helps fill the tiles and keeps the barrier sequence.
+// The same tile sequence for a wavefront that owns no rows (fewer than 32 w
+// rows in the workgroup): it only helps fill the tiles and keeps the barrier
+// sequence.
 template <int F>
 __device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L,
                                                      int k0, int k1) {
@@ -1163,11 +1166,17 @@ __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ 
 
 constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
 
+// The dynamic LDS size above 64 KB must be allowed once per kernel and device
+// (bit d of `done` records device d; setting it twice is harmless).
 template <typename K>
-static hipError_t set_lds(K kernel, bool& done) {  // benign race: the attribute is idempotent
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLds);
-  if (e == hipSuccess) done = true;
+static hipError_t set_lds(K kernel, std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLds);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_relaxed);
   return e;
 }
 
@@ -1186,7 +1195,7 @@ static int head_chunks(const DecodeArgs& a) { return (a.qheads + a.chunk_heads -
 
 template <int F, bool D, int C>
 static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
-  static bool attr_done = false;
+  static std::atomic<unsigned long long> attr_done{0};
   hipError_t e = set_lds(k_decode<F, D, C>, attr_done);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch, head_chunks(a)), dim3(kThreads), kDecodeLds,
@@ -1196,7 +1205,7 @@ static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream)
 
 template <int F, int C>
 static hipError_t launch_flat_one(const DecodeArgs& a, int groups, hipStream_t stream) {
-  static bool attr_done = false;
+  static std::atomic<unsigned long long> attr_done{0};
   hipError_t e = set_lds(k_decode_flat<F, C>, attr_done);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups, head_chunks(a)), dim3(kThreads), kDecodeLds, stream, a);

@@ -24,8 +24,9 @@
  *    are preconditions: entries outside the page pool are skipped rather than
  *    dereferenced, but the results for the affected rows are then unspecified.
  *  - No exception crosses the ABI.  The library is thread-safe for concurrent
- *    calls on different streams (it keeps no mutable global state apart from
- *    a thread-local error string).
+ *    calls on different streams (its only mutable global state is a
+ *    thread-local error string and atomic per-device flags recording that a
+ *    kernel's LDS size limit has been raised).
  */
 #ifndef MLA_LOWBIT_H
 #define MLA_LOWBIT_H
