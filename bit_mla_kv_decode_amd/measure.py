@@ -22,6 +22,10 @@
   python -m bit_mla_kv_decode_amd.measure --parse-counters FETCH.csv WRITE.csv
       per-launch HBM bytes of the decode kernel from FETCH_SIZE / WRITE_SIZE,
       each scaled by what the counter reads for the copy of known size
+  python -m bit_mla_kv_decode_amd.measure --parse-pmc A.csv [B.csv ...]
+      the decode kernel's other counters (median over its dispatches) and
+      the ratios derived from them: MFMA busy share of the SIMD-cycles,
+      VALU/MFMA co-execution, instructions per MFMA, LDS bank conflicts, L2 hits
 """
 from __future__ import annotations
 
@@ -346,13 +350,48 @@ def parse_counters(fetch_csv, write_csv, copy_bytes=1 << 30, packed_bytes=None):
     return rec
 
 
+SIMDS = 256 * 4  # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8         # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs
+
+
+def parse_pmc(paths):
+    vals = {}
+    for p in paths:
+        for k, c, v in _counter_rows(p):
+            if _is_kernel(k, "k_decode_flat"):
+                vals.setdefault(c, []).append(v)
+    m = {c: float(np.median(v)) for c, v in vals.items()}
+    d = {"counters": {c: round(v, 1) for c, v in sorted(m.items())}}
+    g = m.get("GRBM_GUI_ACTIVE")
+    if g and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        # SQ_VALU_MFMA_BUSY_CYCLES sums all SIMDs; GUI-active cycles per XCD times the SIMD count
+        d["gpu_active_cycles"] = round(g / XCDS)
+        d["mfma_busy_share"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (g / XCDS * SIMDS), 4)
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and m.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+        d["coexec_share_of_mfma_busy"] = round(m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+    if m.get("SQ_INSTS_MFMA"):
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS"):
+            if c in m:
+                d[c.lower().replace("sq_insts_", "") + "_per_mfma"] = round(m[c] / m["SQ_INSTS_MFMA"], 3)
+    if m.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in m:
+        d["lds_bank_conflict_per_active_lds_cycle"] = round(m["SQ_LDS_BANK_CONFLICT"] / m["SQ_ACTIVE_INST_LDS"], 4)
+    h, mi = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+    if h is not None and mi is not None and h + mi > 0:
+        d["l2_hit_rate"] = round(h / (h + mi), 4)
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--only", default=",".join(SECTIONS))
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--parse-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--packed-bytes", type=int, default=None)
+    ap.add_argument("--parse-pmc", nargs="+", metavar="CSV")
     args = ap.parse_args()
+    if args.parse_pmc:
+        print(json.dumps(parse_pmc(args.parse_pmc)))
+        return
     if args.parse_counters:
         print(json.dumps(parse_counters(*args.parse_counters, packed_bytes=args.packed_bytes)))
         return
