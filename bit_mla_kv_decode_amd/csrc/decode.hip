@@ -93,49 +93,31 @@ __device__ __forceinline__ unsigned mask_bytes(unsigned w, unsigned m) {
   return r;
 }
 
-// 8 INT4 codes of one dword (element e at bits 4e) -> 8 bf16 values.
-__device__ __forceinline__ bf16x8 dq_int4(unsigned w, float S, float Z) {
-  const unsigned lo = mask_bytes(w, 0x0F0F0F0Fu);        // elements 0, 2, 4, 6
-  const unsigned hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);   // elements 1, 3, 5, 7
-  u32x4 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float a = __builtin_fmaf((float)((lo >> (8 * k)) & 0xFFu), S, Z);
-    const float b = __builtin_fmaf((float)((hi >> (8 * k)) & 0xFFu), S, Z);
-    r[k] = pack_bf16x2(a, b);
-  }
-  return __builtin_bit_cast(bf16x8, r);
+// Codes as floats, two per instruction: a code byte 0..15 read as an OCP fp8
+// e4m3 value is exactly code * 2^-9 (bytes 0..7 are the subnormals m * 2^-9,
+// 8..15 the normals (1 + m / 8) * 2^-6).  With the scale taken as S * 2^9
+// (exact for every fp16 S) the product is code * S exactly, so
+// fma(code * 2^-9, S * 2^9, Z) rounds the same sum as fma(code, S, Z).
+constexpr float kCodeScale = 512.0f;
+// bytes 2 w and 2 w + 1 of x as floats (code * 2^-9); w is a literal after unrolling
+__device__ __forceinline__ f32x2 code_pair(unsigned x, int w) {
+  return w ? __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
 }
 
-// 16 INT2 codes of one dword (element e at bits 2e), all of one group -> 16 bf16 values.
-__device__ __forceinline__ void dq_int2(unsigned w, float S, float Z, bf16x8& o0, bf16x8& o1) {
-  // byte k of (w >> 2j) & 0x03030303 holds element 4k + j
-  const unsigned b0 = mask_bytes(w, 0x03030303u), b1 = mask_bytes(w >> 2, 0x03030303u);
-  const unsigned b2 = mask_bytes(w >> 4, 0x03030303u), b3 = mask_bytes(w >> 6, 0x03030303u);
-  u32x4 r0, r1;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float e0 = __builtin_fmaf((float)((b0 >> (8 * k)) & 0xFFu), S, Z);
-    const float e1 = __builtin_fmaf((float)((b1 >> (8 * k)) & 0xFFu), S, Z);
-    const float e2 = __builtin_fmaf((float)((b2 >> (8 * k)) & 0xFFu), S, Z);
-    const float e3 = __builtin_fmaf((float)((b3 >> (8 * k)) & 0xFFu), S, Z);
-    const unsigned p01 = pack_bf16x2(e0, e1), p23 = pack_bf16x2(e2, e3);
-    if (k < 2) { r0[2 * k] = p01; r0[2 * k + 1] = p23; }
-    else { r1[2 * (k - 2)] = p01; r1[2 * (k - 2) + 1] = p23; }
-  }
-  o0 = __builtin_bit_cast(bf16x8, r0);
-  o1 = __builtin_bit_cast(bf16x8, r1);
-}
-
+// S (scaled by kCodeScale, see code_pair) and Z of a packed fp16 pair
 __device__ __forceinline__ void sz_unpack(unsigned sz, float& S, float& Z) {
-  S = half_bits_to_f32(sz);
+  S = half_bits_to_f32(sz) * kCodeScale;
   Z = half_bits_to_f32(sz >> 16);
 }
 
 // ---------------------------------------------------------------- tile fills
 // A tile is half a page: tokens [32 hp, 32 hp + 32) of one physical page.
-// Thread mapping: t = tid % 32 is the token, cs = tid / 32 selects chunks, so
-// the 32 lanes of a half-wave read 512 contiguous bytes of one code chunk.
+// Thread mapping: lane l = tid % 32 takes token t = rho(l) and cs = tid / 32
+// selects chunks.  The 32 lanes of a half-wave still read 512 contiguous bytes
+// of one code chunk (rho permutes the tokens among them), and since rho is its
+// own inverse the token's tile row rho(t) is l: the lanes of a 16-byte tile
+// write hit consecutive rows, which spread over the LDS banks without
+// conflicts, where writing rows rho(l) cost 8 conflict cycles per write.
 // load(page, hp): issue this thread's global loads into registers.
 // store(tile, nvalid): dequantize into the LDS tile; rows >= nvalid are zero.
 
@@ -156,9 +138,10 @@ template <> struct Fill<kC4R4> {
   bool ok;
   // working state of the dword being converted
   unsigned lo, hi, outw[4];
+  f32x2 flo, fhi;
   float S, Z;
   __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
-    const int t = (threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+    const int t = rho(threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
     ok = page >= 0 && page < num_pages;
     const uint8_t* base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
 #pragma unroll
@@ -173,7 +156,7 @@ template <> struct Fill<kC4R4> {
   // step u: dword p = u / 4 (p < 8: content chunk cs + 8 (p / 4), dword p % 4;
   // p = 8: RoPE), pair q = u % 4 (elements 2q, 2q + 1 of the dword)
   __device__ __forceinline__ void substep(__bf16* tile, int nvalid, int u) {
-    const int t = threadIdx.x & 31, cs = threadIdx.x >> 5;
+    const int l = threadIdx.x & 31, t = rho(l), cs = threadIdx.x >> 5;  // token rho(l) lives in row l
     const int p = u >> 2, q = u & 3;
     if (q == 0) {
       const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
@@ -182,12 +165,16 @@ template <> struct Fill<kC4R4> {
       lo = mask_bytes(w, 0x0F0F0F0Fu);        // elements 0, 2, 4, 6
       hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);   // elements 1, 3, 5, 7
     }
-    const float a = __builtin_fmaf((float)((lo >> (8 * q)) & 0xFFu), S, Z);
-    const float b = __builtin_fmaf((float)((hi >> (8 * q)) & 0xFFu), S, Z);
+    if ((q & 1) == 0) {  // bytes q, q + 1 of lo / hi: elements 2q, 2q + 2 / 2q + 1, 2q + 3
+      flo = code_pair(lo, q >> 1);
+      fhi = code_pair(hi, q >> 1);
+    }
+    const float a = __builtin_fmaf(flo[q & 1], S, Z);
+    const float b = __builtin_fmaf(fhi[q & 1], S, Z);
     outw[q] = pack_bf16x2(a, b);
     if (q == 3) {
       const int chunk = p < 8 ? 4 * (cs + 8 * (p >> 2)) + (p & 3) : 64 + cs;
-      *(u32x4*)(tile + rho(t) * kRow + 8 * chunk) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
+      *(u32x4*)(tile + l * kRow + 8 * chunk) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
     }
   }
   __device__ __forceinline__ void store(__bf16* tile, int nvalid) {
@@ -204,9 +191,10 @@ template <> struct Fill<kC2R4> {
   unsigned r, rsz;
   bool ok;
   unsigned b0, b1, b2, b3, outw[4];
+  f32x2 f0, f1, f2, f3;
   float S, Z;
   __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
-    const int t = (threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+    const int t = rho(threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
     ok = page >= 0 && page < num_pages;
     const uint8_t* base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
     // content chunk cs = channels [64 cs, 64 cs + 64) = groups 2 cs, 2 cs + 1
@@ -219,9 +207,9 @@ template <> struct Fill<kC2R4> {
   // steps 0..31: content dword v = u / 8 (channels [64 cs + 16 v, +16), group
   // 2 cs + v / 2), pair q = u % 8 (elements 2q, 2q + 1); steps 32..35: RoPE
   __device__ __forceinline__ void substep(__bf16* tile, int nvalid, int u) {
-    const int t = threadIdx.x & 31, cs = threadIdx.x >> 5;
+    const int l = threadIdx.x & 31, t = rho(l), cs = threadIdx.x >> 5;  // token rho(l) lives in row l
     const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
-    __bf16* row = tile + rho(t) * kRow;
+    __bf16* row = tile + l * kRow;
     if (u < 32) {
       const int v = u >> 3, q = u & 7;
       if (q == 0) {
@@ -233,11 +221,20 @@ template <> struct Fill<kC2R4> {
         b2 = mask_bytes(w >> 4, 0x03030303u);
         b3 = mask_bytes(w >> 6, 0x03030303u);
       }
-      // elements 2q, 2q + 1 = byte k = q / 2, bit pairs (2q % 4), (2q % 4) + 1
+      // elements 2q, 2q + 1 = byte k = q / 2 of b0, b1 (q even) or b2, b3 (q
+      // odd); the bytes 2 (q / 4), 2 (q / 4) + 1 of all four are converted at
+      // q % 4 = 0 (b0, b1) and 1 (b2, b3) and serve pairs q and q + 2
       const int k = q >> 1;
-      const unsigned ba = (q & 1) ? b2 : b0, bb = (q & 1) ? b3 : b1;
-      const float ea = __builtin_fmaf((float)((ba >> (8 * k)) & 0xFFu), S, Z);
-      const float eb = __builtin_fmaf((float)((bb >> (8 * k)) & 0xFFu), S, Z);
+      if ((q & 3) == 0) {
+        f0 = code_pair(b0, q >> 2);
+        f1 = code_pair(b1, q >> 2);
+      }
+      if ((q & 3) == 1) {
+        f2 = code_pair(b2, q >> 2);
+        f3 = code_pair(b3, q >> 2);
+      }
+      const float ea = __builtin_fmaf((q & 1) ? f2[k & 1] : f0[k & 1], S, Z);
+      const float eb = __builtin_fmaf((q & 1) ? f3[k & 1] : f1[k & 1], S, Z);
       outw[q & 3] = pack_bf16x2(ea, eb);
       if ((q & 3) == 3)
         *(u32x4*)(row + 8 * (8 * cs + 2 * v + (q >> 2))) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
@@ -248,8 +245,12 @@ template <> struct Fill<kC2R4> {
         b0 = mask_bytes(r, 0x0F0F0F0Fu);
         b1 = mask_bytes(r >> 4, 0x0F0F0F0Fu);
       }
-      const float ea = __builtin_fmaf((float)((b0 >> (8 * q)) & 0xFFu), S, Z);
-      const float eb = __builtin_fmaf((float)((b1 >> (8 * q)) & 0xFFu), S, Z);
+      if ((q & 1) == 0) {
+        f0 = code_pair(b0, q >> 1);
+        f1 = code_pair(b1, q >> 1);
+      }
+      const float ea = __builtin_fmaf(f0[q & 1], S, Z);
+      const float eb = __builtin_fmaf(f1[q & 1], S, Z);
       outw[q] = pack_bf16x2(ea, eb);
       if (q == 3) *(u32x4*)(row + 8 * (64 + cs)) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
     }
