@@ -140,18 +140,28 @@ template <> struct Fill<kC4R4> {
   unsigned lo, hi, outw[4];
   f32x2 flo, fhi;
   float S, Z;
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
-    const int t = rho(threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+  const uint8_t* base;  // page of the pending tile
+  int hp;               // its half of the page
+  static constexpr int kLoads = 6;
+  __device__ __forceinline__ void begin(const uint8_t* __restrict__ cache, int64_t page, int half, int64_t num_pages) {
     ok = page >= 0 && page < num_pages;
-    const uint8_t* base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
+    base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
+    hp = half;
+  }
+  // load i of the tile: content chunks cs and cs + 8 (channels [32 j, 32 j + 32),
+  // group j / 2) with their scale/zero, then the RoPE dword and its scale/zero
+  __device__ __forceinline__ void issue(int i) {
+    const int t = rho(threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+    const int j = cs + 8 * (i >> 1);
+    if (i == 0 || i == 2) c[i >> 1] = *(const u32x4*)(base + Lay::kCodesA + (j * kPage + t) * 16);
+    if (i == 1 || i == 3) sz[i >> 1] = *(const unsigned*)(base + Lay::kSzB + ((j >> 1) * kPage + t) * 4);
+    if (i == 4) r = *(const unsigned*)(base + Lay::kCodesC + ((cs >> 2) * kPage + t) * 16 + 4 * (cs & 3));
+    if (i == 5) rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+  }
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int half, int64_t num_pages) {
+    begin(cache, page, half, num_pages);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = cs + 8 * i;  // content chunk = channels [32j, 32j + 32), group j / 2
-      c[i] = *(const u32x4*)(base + Lay::kCodesA + (j * kPage + t) * 16);
-      sz[i] = *(const unsigned*)(base + Lay::kSzB + ((j >> 1) * kPage + t) * 4);
-    }
-    r = *(const unsigned*)(base + Lay::kCodesC + ((cs >> 2) * kPage + t) * 16 + 4 * (cs & 3));
-    rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+    for (int i = 0; i < kLoads; ++i) issue(i);
   }
   // step u: dword p = u / 4 (p < 8: content chunk cs + 8 (p / 4), dword p % 4;
   // p = 8: RoPE), pair q = u % 4 (elements 2q, 2q + 1 of the dword)
@@ -193,16 +203,27 @@ template <> struct Fill<kC2R4> {
   unsigned b0, b1, b2, b3, outw[4];
   f32x2 f0, f1, f2, f3;
   float S, Z;
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
-    const int t = rho(threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+  const uint8_t* base;  // page of the pending tile
+  int hp;               // its half of the page
+  static constexpr int kLoads = 5;
+  __device__ __forceinline__ void begin(const uint8_t* __restrict__ cache, int64_t page, int half, int64_t num_pages) {
     ok = page >= 0 && page < num_pages;
-    const uint8_t* base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
-    // content chunk cs = channels [64 cs, 64 cs + 64) = groups 2 cs, 2 cs + 1
-    c = *(const u32x4*)(base + Lay::kCodesA + (cs * kPage + t) * 16);
-    sz[0] = *(const unsigned*)(base + Lay::kSzB + ((2 * cs) * kPage + t) * 4);
-    sz[1] = *(const unsigned*)(base + Lay::kSzB + ((2 * cs + 1) * kPage + t) * 4);
-    r = *(const unsigned*)(base + Lay::kCodesC + ((cs >> 2) * kPage + t) * 16 + 4 * (cs & 3));
-    rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+    base = cache + (ok ? page : 0) * (int64_t)Lay::kBytes;  // an invalid page reads page 0, zeroed at store
+    hp = half;
+  }
+  // load i of the tile: content chunk cs = channels [64 cs, 64 cs + 64) = groups
+  // 2 cs, 2 cs + 1, their two scale/zero pairs, the RoPE dword and its scale/zero
+  __device__ __forceinline__ void issue(int i) {
+    const int t = rho(threadIdx.x & 31) + 32 * hp, cs = threadIdx.x >> 5;
+    if (i == 0) c = *(const u32x4*)(base + Lay::kCodesA + (cs * kPage + t) * 16);
+    if (i == 1 || i == 2) sz[i - 1] = *(const unsigned*)(base + Lay::kSzB + ((2 * cs + i - 1) * kPage + t) * 4);
+    if (i == 3) r = *(const unsigned*)(base + Lay::kCodesC + ((cs >> 2) * kPage + t) * 16 + 4 * (cs & 3));
+    if (i == 4) rsz = *(const unsigned*)(base + Lay::kSzD + t * 4);
+  }
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int half, int64_t num_pages) {
+    begin(cache, page, half, num_pages);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) issue(i);
   }
   // steps 0..31: content dword v = u / 8 (channels [64 cs + 16 v, +16), group
   // 2 cs + v / 2), pair q = u % 8 (elements 2q, 2q + 1); steps 32..35: RoPE
@@ -267,12 +288,17 @@ template <> struct Fill<kC2R4> {
 // replaced by zeros.
 template <> struct Fill<kBF16> {
   static constexpr int kSubsteps = 0;
+  static constexpr int kLoads = 0;
   const uint8_t* base;
   bool ok;
   __device__ __forceinline__ void substep(__bf16*, int, int) {}
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
+  __device__ __forceinline__ void begin(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
     ok = page >= 0 && page < num_pages;
     base = cache + (ok ? page : 0) * (int64_t)PageLayout<kBF16>::kBytes + hp * (kTileTok * kD * 2);
+  }
+  __device__ __forceinline__ void issue(int) {}
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ cache, int64_t page, int hp, int64_t num_pages) {
+    begin(cache, page, hp, num_pages);
   }
   __device__ __forceinline__ void store(__bf16* tile, int nvalid) const {
 #pragma unroll
@@ -400,9 +426,13 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
     __bf16* tile = smem + ((k - k0) & 1) * kTile;
     __bf16* next = smem + ((k - k0 + 1) & 1) * kTile;
     // next tile's loads (the last iteration reloads its own tile: harmless,
-    // keeps the loop body a single basic block so VALU and MFMA interleave)
+    // keeps the loop body a single basic block so VALU and MFMA interleave),
+    // issued one every kLoadEvery k-steps of Q.K^T below: a burst of them
+    // would hold the wavefront's in-order issue while the memory pipeline
+    // takes them, with no MFMA running alongside
     const int kn = min(k + 1, k1 - 1);
-    fill.load(a.cache, win.page_of(kn), kn & 1, a.num_pages);
+    fill.begin(a.cache, win.page_of(kn), kn & 1, a.num_pages);
+    constexpr int kLoadEvery = 3;
 
     // ---- S^T = khat . q^T for the 32 tokens of the tile.  Operands are read
     //      4 k-steps ahead; scheduling barriers pin that order so LDS latency
@@ -422,6 +452,7 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
       __builtin_amdgcn_sched_barrier(0);
       if (ks + 4 < 36) kv[ks & 3] = *(const bf16x8*)(arow + 16 * (ks + 4));
       if (q_in_lds(ks) && ks + 4 < 32) qv[(ks >> 1) & 1] = *(const bf16x8*)(qrow + 16 * ((ks >> 1) + 2));
+      if (ks % kLoadEvery == 1 && ks / kLoadEvery < Fill<F>::kLoads) fill.issue(ks / kLoadEvery);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- softmax weights (log2 domain); reg r is token 8 (r / 4) + 4 hi + r % 4
