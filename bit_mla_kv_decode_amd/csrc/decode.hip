@@ -974,7 +974,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
 // (workgroup, sequence) piece is written to partial slot w + b: the slots of
 // one sequence are consecutive, and the workgroup holding a sequence's first
 // page records (first slot, count) in a.meta[b].
-__device__ __forceinline__ int64_t share_start(int64_t w, int64_t T, int64_t G) { return (w * T) / G; }
+// floor(w T / G) in double precision, exact here: w <= G <= 256 and T < 2^44
+// pages keep w T below 2^53, and a quotient that is not an integer lies at
+// least 1 / G away from one, far beyond the division's rounding error.
+__device__ __forceinline__ int64_t share_start(int64_t w, int64_t T, int64_t G) {
+  return (int64_t)floor((double)(w * T) / (double)G);
+}
 
 __device__ __forceinline__ int opaque_lane() {
   int l;
@@ -1000,7 +1005,14 @@ struct FlatWalk {
   int len[64];
   long long off[64];
   int piece[4];          // sequence (-1: share done), length, first tile, end tile
+  int lens[kThreads];    // clamped lengths of sequences 0 .. kThreads - 1
 };
+
+// Clamped length of sequence b < a.batch: from the workgroup's copy for the
+// first kThreads sequences, else from global memory.
+__device__ __forceinline__ int walk_len(const DecodeArgs& a, const FlatWalk& walk, int b) {
+  return b < kThreads ? walk.lens[b] : clamped_len(a, b);
+}
 
 // Wavefront 0 only (all 64 lanes): find the next piece of the share and
 // publish it in walk.piece.  A sequence whose first page lies in the share
@@ -1035,7 +1047,7 @@ __device__ __forceinline__ void flat_next_piece(const DecodeArgs& a, FlatWalk& w
     j = 0;
     // scan the chunk's page counts (inclusive prefix sum over the wavefront)
     const int b = b0 + ln;
-    const int L = b < a.batch ? clamped_len(a, b) : 0;
+    const int L = b < a.batch ? walk_len(a, walk, b) : 0;
     const int n = (L + kPage - 1) / kPage;
     int incl = n;
 #pragma unroll
@@ -1080,19 +1092,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_flat(const DecodeArgs a)
   __shared__ FlatWalk walk;
   const int tid = threadIdx.x;
   const int64_t w = blockIdx.x;
+  // one read of the lengths: the first kThreads stay in LDS for the walk
+  const int len_t = tid < a.batch ? clamped_len(a, tid) : 0;
+  walk.lens[tid] = len_t;
   if (tid == 0) s_total = 0;
   __syncthreads();
   {
-    unsigned long long part = 0;
-    for (int b = tid; b < a.batch; b += kThreads) part += (clamped_len(a, b) + kPage - 1) / kPage;
-    atomicAdd(&s_total, part);
+    unsigned long long part = (len_t + kPage - 1) / kPage;
+    for (int b = tid + kThreads; b < a.batch; b += kThreads) part += (clamped_len(a, b) + kPage - 1) / kPage;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d);
+    if ((tid & 63) == 0) atomicAdd(&s_total, part);
   }
   __syncthreads();
   const int64_t T = (int64_t)uniform64(s_total);
   // empty sequences own no slots: record (0, 0) for them (strided over
   // workgroups; head chunk 0 writes all slot records)
   for (int b = (int)w * kThreads + tid; blockIdx.y == 0 && b < a.batch; b += (int)gridDim.x * kThreads)
-    if (clamped_len(a, b) == 0) {
+    if ((b == tid ? len_t : clamped_len(a, b)) == 0) {
       a.meta[2 * b] = 0;
       a.meta[2 * b + 1] = 0;
     }
