@@ -171,6 +171,29 @@ def section_peaks():
     emit({"row": "peak_mfma_bf16_32x32x16", "TFLOPs": round(mf / 1e12, 1), "frac_of_2p5PF": round(mf / MFMA_BF16_PEAK, 4)})
     del src, dst
     torch.cuda.empty_cache()
+    # cycle costs, one wavefront per SIMD on every compute unit (256 workgroups)
+    G = 256
+    cyc = torch.zeros(2 * G, dtype=torch.int64, device="cuda")
+    for chains in (1, 2):
+        for nv in ((0,) if chains == 1 else (0, 2, 4, 6, 8, 12)):
+            iters = 20000 // chains
+            peaks.mfma_cycles(G, iters, chains, nv, cyc, sink, st)  # warm-up
+            peaks.mfma_cycles(G, iters, chains, nv, cyc, sink, st)
+            torch.cuda.synchronize()
+            c = cyc.view(G, 2).double().cpu().numpy()
+            per = float(np.median(c[:, 0])) / (iters * chains)
+            ghz = float(np.median(c[:, 0] / c[:, 1])) * 0.1
+            emit({"row": "mfma_cycles", "chains": chains, "valu_per_mfma": nv,
+                  "cycles_per_mfma": round(per, 1), "shader_clock_GHz": round(ghz, 2)})
+    lsink = torch.zeros(G * 512, dtype=torch.int32, device="cuda")
+    for write in (False, True):
+        for waves in (1, 2):
+            peaks.lds(G, waves, write, 20000, cyc, lsink, st)
+            by = peaks.lds(G, waves, write, 20000, cyc, lsink, st)
+            torch.cuda.synchronize()
+            c = float(np.median(cyc[:G].double().cpu().numpy()))
+            emit({"row": "lds_bandwidth", "op": "write_b128" if write else "read_b128", "waves_per_simd": waves,
+                  "bytes_per_cycle_per_cu": round(by / c, 1)})
 
 
 def section_configs():

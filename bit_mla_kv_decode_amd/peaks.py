@@ -1,6 +1,7 @@
 """ctypes binding of libmla_peaks.so: the practical-peak microbenchmarks
-(streaming HBM read, plain copy, dense bf16 MFMA loop) the decode kernels
-are measured against."""
+(streaming HBM read, plain copy, dense bf16 MFMA loop, MFMA cycle costs with
+VALU work between the MFMAs, LDS bandwidth) the decode kernels are measured
+against."""
 from __future__ import annotations
 
 import ctypes
@@ -20,6 +21,8 @@ def load_library():
         L.peak_copy.argtypes, L.peak_copy.restype = [vp, vp, sz, vp], i32
         L.peak_read.argtypes, L.peak_read.restype = [vp, sz, i32, vp, vp], i32
         L.peak_mfma_bf16.argtypes, L.peak_mfma_bf16.restype = [i32, i32, vp, vp], i32
+        L.peak_mfma_cycles.argtypes, L.peak_mfma_cycles.restype = [i32, i32, i32, i32, vp, vp, vp], i32
+        L.peak_lds.argtypes, L.peak_lds.restype = [i32, i32, i32, i32, vp, vp, vp], i32
         _lib = L
     return _lib
 
@@ -49,3 +52,22 @@ def mfma_bf16(groups, iters, sink, stream=None):
     assert sink.numel() >= groups * 256
     _ck(load_library().peak_mfma_bf16(groups, iters, sink.data_ptr(), _s(stream)), "peak_mfma_bf16")
     return groups * 4 * iters * 4 * 32768
+
+
+def mfma_cycles(groups, iters, chains, valu_per_mfma, cycles, sink, stream=None):
+    """Time `iters` rounds of `chains` MFMA chains, `valu_per_mfma` FMAs after each
+    MFMA; cycles (int64 device tensor of 2 * groups) receives per workgroup the
+    shader-clock cycles and the 100 MHz reference ticks of the loop."""
+    assert cycles.numel() >= 2 * groups and sink.numel() >= groups * 256
+    _ck(load_library().peak_mfma_cycles(groups, iters, chains, valu_per_mfma, cycles.data_ptr(), sink.data_ptr(),
+                                        _s(stream)), "peak_mfma_cycles")
+
+
+def lds(groups, waves_per_simd, write, iters, cycles, sink, stream=None):
+    """LDS read (write=False) or write bandwidth loop; cycles (int64 device tensor
+    of groups) receives each workgroup's shader-clock cycles.  Returns the
+    bytes one workgroup moves."""
+    assert cycles.numel() >= groups and sink.numel() >= groups * 256 * waves_per_simd
+    _ck(load_library().peak_lds(groups, waves_per_simd, int(write), iters, cycles.data_ptr(), sink.data_ptr(),
+                                _s(stream)), "peak_lds")
+    return iters * 8 * 16 * 256 * waves_per_simd

@@ -35,13 +35,18 @@ def test_peaks_header_symbols_are_exported():
     from bit_mla_kv_decode_amd import peaks
     lib = peaks.load_library()
     names = _declared(os.path.join(ROOT, "include", "mla_peaks.h"), "peak_")
-    assert names == ["peak_copy", "peak_mfma_bf16", "peak_read"]
+    assert names == ["peak_copy", "peak_lds", "peak_mfma_bf16", "peak_mfma_cycles", "peak_read"]
     for n in names:
         assert hasattr(lib, n), n
-    # host-side argument checks (no launch): misaligned or ragged sizes are refused
+    # host-side argument checks (no launch): misaligned or ragged sizes, unsupported shapes are refused
     assert lib.peak_copy(A, A2, 17, None) != 0
     assert lib.peak_read(A, 1000, 256, A2, None) != 0
     assert lib.peak_mfma_bf16(0, 10, A2, None) != 0
+    assert lib.peak_mfma_cycles(256, 10, 3, 0, A, A2, None) != 0     # 1 or 2 chains
+    assert lib.peak_mfma_cycles(256, 10, 2, 5, A, A2, None) != 0     # 0, 2, 4, 6, 8 or 12 FMAs
+    assert lib.peak_mfma_cycles(0, 10, 2, 0, A, A2, None) != 0
+    assert lib.peak_lds(256, 3, 0, 10, A, A2, None) != 0             # 1 or 2 wavefronts per SIMD
+    assert lib.peak_lds(0, 1, 0, 10, A, A2, None) != 0
 
 
 def test_format_queries():
