@@ -66,7 +66,7 @@ def build_workload(w, device, replicas):
 
 
 KERNEL_SOURCES = ("bit_mla_kv_decode_amd/csrc/decode.hip", "bit_mla_kv_decode_amd/csrc/common.h",
-                  "bit_mla_kv_decode_amd/csrc/kernels.h")
+                  "bit_mla_kv_decode_amd/csrc/kernels.h", "bit_mla_kv_decode_amd/csrc/append.h")
 
 
 def kernel_source_sha256():
@@ -92,6 +92,19 @@ def counted_traffic(workload, fmt):
     if not sha or not val or sha.group(1) != kernel_source_sha256():
         return None
     return int(val.group(1))
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w, seqs=8):
@@ -121,6 +134,7 @@ def cpu_baseline(w, seqs=8):
     oracle.decode(fmt, q[:1], cache, npages, bt[:1], np.array([n1], np.int32), w.softmax_scale, nthreads=1)
     dt1 = time.perf_counter() - t
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "host": {"cpu_model": _cpu_model(), "cpus_visible": os.cpu_count()},
             "sample": "%d of %d sequences (%d tokens), all %d heads, decode only (fp64), %.1f s"
                       % (len(lens), w.batch, tokens, w.heads, dt),
             "single_thread": {"value": round(n1 * tb / dt1 / 1e9, 6), "unit": "GB/s",
