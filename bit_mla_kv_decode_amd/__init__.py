@@ -15,7 +15,7 @@ import os
 __all__ = [
     "FORMATS", "MlaError", "format_struct", "load_library",
     "mla_token_bytes", "mla_page_bytes", "mla_quant_append", "mla_decode_num_splits",
-    "mla_decode_workspace_bytes", "mla_decode_lowbit", "mla_decode_partial", "mla_decode_combine",
+    "mla_decode_workspace_bytes", "mla_decode_partial_slots", "mla_decode_lowbit", "mla_decode_partial", "mla_decode_combine",
     "mla_decode_append_lowbit", "mla_decode_append_partial", "mla_decode_multi_lowbit",
     "mla_decode_multi_partial", "mla_absorb_q", "mla_project_out",
     "mla_last_error", "alloc_cache",
@@ -69,6 +69,7 @@ def load_library():
         "mla_quant_append": (ctypes.c_int, [FP, P, P, P, I32, P, I64, P]),
         "mla_decode_num_splits": (I32, [FP, I32, I32, I32]),
         "mla_decode_workspace_bytes": (SZ, [FP, I32, I32, I32]),
+        "mla_decode_partial_slots": (I64, [FP, I32, I32, I32]),
         "mla_decode_lowbit": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P, P, P]),
         "mla_decode_partial": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P]),
         "mla_decode_combine": (ctypes.c_int, [FP, I32, I32, I32, P, SZ, P, P, P]),
@@ -163,6 +164,13 @@ def mla_decode_num_splits(fmt, batch: int, num_heads: int, max_seq_len: int) -> 
 def mla_decode_workspace_bytes(fmt, batch: int, num_heads: int, num_splits: int) -> int:
     return int(load_library().mla_decode_workspace_bytes(ctypes.byref(format_struct(fmt)), batch, num_heads,
                                                          num_splits))
+
+
+def mla_decode_partial_slots(fmt, batch: int, num_heads: int, num_splits: int) -> int:
+    """Partial slots of the decode workspace: batch * num_splits, or the balanced
+    partition's workgroups + batch for num_splits = 0."""
+    return int(load_library().mla_decode_partial_slots(ctypes.byref(format_struct(fmt)), batch, num_heads,
+                                                       num_splits))
 
 
 def _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages):
@@ -331,10 +339,11 @@ def workspace_views(fmt, workspace, batch, num_heads, num_splits):
 
 def balanced_workspace_views(fmt, workspace, batch, num_heads):
     """Views of a workspace written with num_splits = 0: fp32 o_part
-    [256 + B, H, 512], fp32 lse_part [256 + B, H] (slot w + b holds workgroup
-    w's piece of sequence b) and int32 meta [B, 2] (first slot, slot count)."""
+    [G + B, H, 512], fp32 lse_part [G + B, H] (slot w + b holds workgroup
+    w's piece of sequence b; G + B from mla_decode_partial_slots) and int32
+    meta [B, 2] (first slot, slot count)."""
     import torch
-    slots = 256 + batch
+    slots = mla_decode_partial_slots(fmt, batch, num_heads, 0)
     n_o = slots * num_heads * 512
     o_bytes = (n_o * 4 + 255) // 256 * 256
     l_bytes = (slots * num_heads * 4 + 255) // 256 * 256

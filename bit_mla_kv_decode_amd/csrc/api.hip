@@ -52,32 +52,36 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workgroups that run at once: one per compute unit, two where the decode
+// kernel splits channels (<= 32 rows per sequence, quantized formats).
+int resident_groups(int fmt, int rows) { return kComputeUnits * mla::workgroups_per_cu(fmt, rows); }
+
 // Partial-row slots: batch * splits per-sequence splits, or, for the balanced
 // partition (splits == 0), one per (workgroup, sequence) piece: at most
-// kFlatGroups + batch - 1.
-constexpr int kFlatGroups = kComputeUnits;
-size_t slot_count(int batch, int splits) {
-  return splits > 0 ? (size_t)batch * splits : (size_t)kFlatGroups + batch;
+// resident_groups + batch - 1.
+size_t slot_count(int fmt, int batch, int rows, int splits) {
+  return splits > 0 ? (size_t)batch * splits : (size_t)resident_groups(fmt, rows) + batch;
 }
 
-size_t partial_o_bytes(int batch, int heads, int splits) {
-  return align_up(slot_count(batch, splits) * heads * mla::kDc * sizeof(float), 256);
+size_t partial_o_bytes(int fmt, int batch, int rows, int splits) {
+  return align_up(slot_count(fmt, batch, rows, splits) * rows * mla::kDc * sizeof(float), 256);
 }
 
-size_t partial_lse_bytes(int batch, int heads, int splits) {
-  return align_up(slot_count(batch, splits) * heads * sizeof(float), 256);
+size_t partial_lse_bytes(int fmt, int batch, int rows, int splits) {
+  return align_up(slot_count(fmt, batch, rows, splits) * rows * sizeof(float), 256);
 }
 
-size_t workspace_bytes(int batch, int heads, int splits) {
-  size_t n = partial_o_bytes(batch, heads, splits) + partial_lse_bytes(batch, heads, splits);
+size_t workspace_bytes(int fmt, int batch, int rows, int splits) {
+  size_t n = partial_o_bytes(fmt, batch, rows, splits) + partial_lse_bytes(fmt, batch, rows, splits);
   if (splits == 0) n += align_up((size_t)batch * 2 * sizeof(int), 256);  // per-sequence (first slot, count)
   return n;
 }
 
-int auto_splits(int batch, int max_seq_len) {
+int auto_splits(int fmt, int rows, int batch, int max_seq_len) {
   const int pages = (max_seq_len + mla::kPage - 1) / mla::kPage;
   if (batch <= 0 || pages <= 1) return 1;
-  int s = (kComputeUnits + batch - 1) / batch;                       // fill the compute units
+  const int units = resident_groups(fmt, rows);
+  int s = (units + batch - 1) / batch;                               // fill the compute units
   const int s_len = (pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;  // bound the longest split
   if (s_len > s) s = s_len;
   if (s > kMaxSplits) s = kMaxSplits;
@@ -151,9 +155,9 @@ mla::DecodeArgs make_args(const void* q, const void* cache, int64_t num_pages, c
   if (workspace) {
     const int rows = sh.s_q * num_heads;
     a.o_part = (float*)workspace;
-    a.lse_part = (float*)((char*)workspace + partial_o_bytes(batch, rows, sh.splits));
-    a.meta = (int*)((char*)workspace + partial_o_bytes(batch, rows, sh.splits) +
-                    partial_lse_bytes(batch, rows, sh.splits));
+    a.lse_part = (float*)((char*)workspace + partial_o_bytes(sh.fmt, batch, rows, sh.splits));
+    a.meta = (int*)((char*)workspace + partial_o_bytes(sh.fmt, batch, rows, sh.splits) +
+                    partial_lse_bytes(sh.fmt, batch, rows, sh.splits));
   }
   return a;
 }
@@ -186,14 +190,15 @@ mla_status_t decode_partial(const mla_format_t* fmt, const void* q_bf16, int32_t
   const int rows = s_q * num_heads;
   if (!workspace || !aligned(workspace, 256))
     return fail(MLA_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
-  if (ws_bytes < workspace_bytes(batch, rows, sh.splits))
+  if (ws_bytes < workspace_bytes(sh.fmt, batch, rows, sh.splits))
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
-                workspace_bytes(batch, rows, sh.splits));
+                workspace_bytes(sh.fmt, batch, rows, sh.splits));
   mla::DecodeArgs a = make_args(q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
                                 max_pages_per_seq, softmax_scale, sh, workspace);
   set_append(a, ap);
   hipError_t e = sh.splits > 0 ? mla::launch_decode(sh.fmt, false, a, batch, (hipStream_t)stream)
-                               : mla::launch_decode_flat(sh.fmt, a, kFlatGroups, (hipStream_t)stream);
+                               : mla::launch_decode_flat(sh.fmt, a, resident_groups(sh.fmt, rows),
+                                                         (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return MLA_OK;
 }
@@ -210,12 +215,14 @@ mla_status_t decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_
   if (!workspace || !out_bf16) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
   if (!aligned(workspace, 256) || !aligned(out_bf16, 16) || (lse_out && !aligned(lse_out, 4)))
     return fail(MLA_ERR_INVALID_ARG, "misaligned workspace or output");
-  if (ws_bytes < workspace_bytes(batch, num_heads, num_splits))
+  const int id = format_id(fmt);
+  if (ws_bytes < workspace_bytes(id, batch, num_heads, num_splits))
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
-                workspace_bytes(batch, num_heads, num_splits));
+                workspace_bytes(id, batch, num_heads, num_splits));
   const float* o_part = (const float*)workspace;
-  const float* lse_part = (const float*)((const char*)workspace + partial_o_bytes(batch, num_heads, num_splits));
-  const int* meta = (const int*)((const char*)lse_part + partial_lse_bytes(batch, num_heads, num_splits));
+  const float* lse_part =
+      (const float*)((const char*)workspace + partial_o_bytes(id, batch, num_heads, num_splits));
+  const int* meta = (const int*)((const char*)lse_part + partial_lse_bytes(id, batch, num_heads, num_splits));
   hipError_t e = num_splits > 0
                      ? mla::launch_combine(o_part, lse_part, batch, num_heads, num_splits, (__bf16*)out_bf16, lse_out,
                                            (hipStream_t)stream)
@@ -285,14 +292,18 @@ mla_status_t mla_quant_append(const mla_format_t* fmt, const void* latent_bf16, 
 }
 
 int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t max_seq_len) {
-  (void)fmt;
-  (void)num_heads;
-  return auto_splits(batch, max_seq_len);
+  const int id = format_id(fmt);
+  return auto_splits(id < 0 ? mla::kBF16 : id, num_heads, batch, max_seq_len);
 }
 
 size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits) {
   if (format_id(fmt) < 0 || batch < 0 || num_heads < 1 || num_splits < 0 || num_splits > kMaxSplits) return 0;
-  return workspace_bytes(batch, num_heads, num_splits);
+  return workspace_bytes(format_id(fmt), batch, num_heads, num_splits);
+}
+
+int64_t mla_decode_partial_slots(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits) {
+  if (format_id(fmt) < 0 || batch < 0 || num_heads < 1 || num_splits < 0 || num_splits > kMaxSplits) return 0;
+  return (int64_t)slot_count(format_id(fmt), batch, num_heads, num_splits);
 }
 
 mla_status_t mla_decode_partial(const mla_format_t* fmt, const void* q_bf16, const void* cache, int64_t num_pages,

@@ -576,8 +576,9 @@ __device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16
 // and channels [c 512 / C, (c + 1) 512 / C) of P.V (O in 256 / C
 // accumulators).  The partial logits go through LDS; every wavefront of the
 // group adds the C parts in the same order, so all of them hold bitwise the
-// same S, weights and denominator.  The freed registers hold the packed bytes
-// of D tiles ahead instead of one.
+// same S, weights and denominator.  The packed bytes of the next D tiles are
+// kept in registers; with two workgroups per compute unit (the launch bound
+// below) D = 1: the other workgroup's work covers the load latency.
 template <int C> struct CsAcc {
   f32x16 o[16 / C];
   float l_sum, m_ref, m_seen;
@@ -593,7 +594,11 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
   constexpr int NK = 36 / C, NCT = 16 / C;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5;
   const int part = wave % C, group = wave / C;
-  float* xch = (float*)(smem + 2 * kTile);  // [wave][4][lane][4] floats
+  // the partial logits go through the tile buffer that receives the next
+  // tile: it is free from the end of the previous P.V until this tile's
+  // dequantization starts (after the barrier that follows the exchange), so
+  // the pass needs only the two tile buffers and two workgroups fit on a
+  // compute unit
   const int g = lane >> 4, i16 = lane & 15;
   const int tr_row0 = 4 * (i16 >> 2) + (g >> 1);
   const int tr_chunk = 2 * (g & 1) + ((i16 & 3) >> 1);
@@ -645,6 +650,7 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       __builtin_amdgcn_sched_barrier(0);
       // ---- sum the group's C parts in part order
       {
+        float* xch = (float*)next;  // [wave][4][lane][4] floats
         float* xw = xch + wave * kXchFloats + 4 * lane;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) *(f32x4*)(xw + 256 * j4) = (f32x4){s[4 * j4], s[4 * j4 + 1], s[4 * j4 + 2], s[4 * j4 + 3]};
@@ -660,6 +666,7 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
           s[4 * j4 + 2] = v[2];
           s[4 * j4 + 3] = v[3];
         }
+        __syncthreads();  // every wavefront has read the exchange before the dequantization writes over it
       }
       // ---- softmax weights, as in split_pass
       if ((k + 1) * kTileTok > limit_min) {
@@ -864,7 +871,7 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem,
     float m_fixed = 0.0f;
     for (int pass = 0;; ++pass) {
       CsAcc<C> acc;
-      const bool lifted = split_pass_cs<F, C, 3>(a, smem, bt, L, k0, k1, qr, row.limit, fixed, m_fixed, acc);
+      const bool lifted = split_pass_cs<F, C, 1>(a, smem, bt, L, k0, k1, qr, row.limit, fixed, m_fixed, acc);
       const bool redo = __syncthreads_or(lifted);
       if (!redo || pass > 0) {
         write_split_cs<kDirect, C>(a, b, slot, row, acc);
@@ -939,7 +946,7 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
 // Per-sequence splits: workgroup (split, b) covers pages [split * P, (split + 1) * P)
 // of sequence b, the last split running to the end of the sequence.
 template <int F, bool kDirect, int C>
-__global__ __launch_bounds__(kThreads, 1) void k_decode(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, C > 1 ? 2 : 1) void k_decode(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   const int split = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
   const int tid = threadIdx.x;
@@ -1087,7 +1094,7 @@ __device__ __forceinline__ void flat_next_piece(const DecodeArgs& a, FlatWalk& w
 }
 
 template <int F, int C>
-__global__ __launch_bounds__(kThreads, 1) void k_decode_flat(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, C > 1 ? 2 : 1) void k_decode_flat(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   __shared__ unsigned long long s_total;
   __shared__ FlatWalk walk;
@@ -1214,7 +1221,12 @@ __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ 
 
 // ---------------------------------------------------------------- launchers
 
+// One head group per wavefront: two tiles and the LDS share of q, one
+// workgroup per compute unit.  Channel split: the two tiles only (the logit
+// exchange reuses the tile being refilled), two workgroups per compute unit.
 constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
+constexpr size_t kDecodeLdsCs = 2 * (size_t)kTile * sizeof(__bf16);                 // 74752 bytes
+template <int C> constexpr size_t decode_lds() { return C > 1 ? kDecodeLdsCs : kDecodeLds; }
 
 // The dynamic LDS size above 64 KB must be allowed once per kernel and device
 // (bit d of `done` records device d; setting it twice is harmless).
@@ -1240,6 +1252,8 @@ static int channel_split(int fmt, int rows) {
   return rows <= 32 ? 4 : 1;
 }
 
+int workgroups_per_cu(int fmt, int rows) { return channel_split(fmt, rows) > 1 ? 2 : 1; }
+
 // Head chunks of a launch (grid dimension): s_q * chunk_heads rows each.
 static int head_chunks(const DecodeArgs& a) { return (a.qheads + a.chunk_heads - 1) / a.chunk_heads; }
 
@@ -1248,7 +1262,7 @@ static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream)
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t e = set_lds(k_decode<F, D, C>, attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch, head_chunks(a)), dim3(kThreads), kDecodeLds,
+  hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch, head_chunks(a)), dim3(kThreads), decode_lds<C>(),
                      stream, a);
   return hipGetLastError();
 }
@@ -1258,7 +1272,7 @@ static hipError_t launch_flat_one(const DecodeArgs& a, int groups, hipStream_t s
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t e = set_lds(k_decode_flat<F, C>, attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups, head_chunks(a)), dim3(kThreads), kDecodeLds, stream, a);
+  hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups, head_chunks(a)), dim3(kThreads), decode_lds<C>(), stream, a);
   return hipGetLastError();
 }
 

@@ -35,6 +35,10 @@ hipError_t launch_quant_append(int fmt, const void* latent, const void* rope, co
                                void* cache, int64_t num_pages, hipStream_t stream);
 hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream);
+// Decode workgroups one compute unit holds at once for `rows` rows per
+// sequence: 2 where the kernel splits channels (quantized formats, <= 32
+// rows), else 1.  The balanced partition launches this many per unit.
+int workgroups_per_cu(int fmt, int rows);
 hipError_t launch_combine_flat(const float* o_part, const float* lse_part, const int* meta, int batch, int heads,
                                __bf16* out, float* lse_out, hipStream_t stream);
 // q [B, H, 576] = [q_nope W_UK^T | q_pe] per head; o [B, H, 128] = out W_UV^T per head

@@ -98,7 +98,8 @@ mla_status_t mla_quant_append(const mla_format_t* fmt,
                               void* cache, int64_t num_pages, void* stream);
 
 /* A per-sequence split count suited to this shape (from the batch size, the
- * longest sequence and the number of compute units), for callers that want
+ * longest sequence and the workgroups the compute units hold at once: two
+ * per unit for the quantized formats at <= 32 heads), for callers that want
  * the fixed-split mode; always in [1, 64].  num_splits = 0 (the balanced
  * partition) needs no such choice. */
 int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
@@ -108,10 +109,18 @@ int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t nu
  * (0 for an invalid argument).  num_splits = S >= 1: fp32 partial outputs
  * [batch, S, num_heads, d_c], then fp32 partial log-sum-exps
  * [batch, S, num_heads].  num_splits = 0: the same two arrays over
- * 256 + batch partial slots, then int32 [batch, 2] (first slot, slot count)
- * per sequence.  Each array starts 256-byte aligned. */
+ * G + batch partial slots, then int32 [batch, 2] (first slot, slot count)
+ * per sequence, where G (the balanced partition's workgroups) is 512 for the
+ * quantized formats at <= 32 rows per sequence (two workgroups per compute
+ * unit) and 256 otherwise.  Each array starts 256-byte aligned. */
 size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
                                   int32_t num_splits);
+
+/* Partial slots in that workspace: batch * num_splits, or G + batch for
+ * num_splits = 0 (0 for an invalid argument).  num_heads is the rows per
+ * sequence, as for mla_decode_workspace_bytes. */
+int64_t mla_decode_partial_slots(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
+                                 int32_t num_splits);
 
 /* Decode attention over the packed cache, for one query token per sequence:
  *   out[b, h, :] = sum_t softmax_t(scale * <q[b,h,:], khat[t,:]>) * khat[t, :d_c]
@@ -130,8 +139,10 @@ size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_
  *   max_pages_per_seq  1..2^24
  *   max_seq_len   host upper bound on seq_lens (sizes the fixed splits)
  *   num_splits    0 = balanced: the batch's pages, in sequence order, are cut
- *                 into min(256, pages) equal shares, one workgroup per share
- *                 (one per compute unit), whatever the length mix; 1..64 = every
+ *                 into min(G, pages) equal shares, one workgroup per share
+ *                 (G = 256, one per compute unit, or 512 for the quantized
+ *                 formats at <= 32 heads, two per unit), whatever the length
+ *                 mix; 1..64 = every
  *                 sequence cut into that many contiguous page ranges.  Either
  *                 way the pieces are merged by log-sum-exp
  *   workspace     >= mla_decode_workspace_bytes(fmt, batch, num_heads,
@@ -223,7 +234,7 @@ mla_status_t mla_decode_multi_partial(const mla_format_t* fmt, const void* q_bf1
  * num_splits = S >= 1, split s of sequence b covers pages [s * P, (s + 1) * P)
  * with P = ceil(ceil(max_seq_len / page_size) / S), the last split running to
  * the end of the sequence.  With num_splits = 0, T = the batch's pages in all
- * and G = min(256, T), workgroup w < G takes pages
+ * and G = min(512 or 256 as for mla_decode_workspace_bytes, T), workgroup w < G takes pages
  * [floor(w * T / G), floor((w + 1) * T / G)) of the concatenation of all
  * sequences' pages (never empty), writes its piece of sequence b to slot
  * w + b, and records each sequence's (first slot, slot count) in the

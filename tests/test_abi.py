@@ -71,11 +71,20 @@ def test_split_heuristic_and_workspace():
         n = B * S * H
         expect = (n * 512 * 4 + 255) // 256 * 256 + (n * 4 + 255) // 256 * 256
         assert mla.mla_decode_workspace_bytes(f, B, H, S) == expect
-    # balanced partition: 256 + B slots, then int32 (first slot, count) per sequence
-    for B, H in [(8, 128), (1, 1), (300, 17)]:
-        n = (256 + B) * H
+    # balanced partition: G + B slots, then int32 (first slot, count) per sequence; G = 512
+    # workgroups (two per compute unit) where the quantized formats split channels (<= 32 rows)
+    for fm, B, H, G in [(f, 8, 128, 256), (f, 1, 1, 512), (f, 300, 17, 512), ("C2R4", 4, 32, 512),
+                        ("C2R4", 4, 33, 256), ("BF16", 1, 1, 256), ("BF16", 8, 128, 256)]:
+        n = (G + B) * H
         expect = (n * 512 * 4 + 255) // 256 * 256 + (n * 4 + 255) // 256 * 256 + (B * 8 + 255) // 256 * 256
-        assert mla.mla_decode_workspace_bytes(f, B, H, 0) == expect
+        assert mla.mla_decode_workspace_bytes(fm, B, H, 0) == expect, (fm, B, H)
+        assert mla.mla_decode_partial_slots(fm, B, H, 0) == G + B
+    assert mla.mla_decode_partial_slots(f, 8, 128, 32) == 256
+    assert mla.mla_decode_partial_slots(f, 8, 0, 0) == 0
+    # fixed splits fill the resident workgroups: 512 at <= 32 heads
+    assert mla.mla_decode_num_splits(f, 8, 16, 131072) == 64
+    assert mla.mla_decode_num_splits(f, 16, 16, 131072) == 32
+    assert mla.mla_decode_num_splits("BF16", 16, 16, 131072) == 16
     assert mla.mla_decode_workspace_bytes(f, 8, 0, 4) == 0
     assert mla.mla_decode_workspace_bytes(f, 8, 128, -1) == 0
     assert mla.mla_decode_workspace_bytes(f, 8, 128, 65) == 0

@@ -244,7 +244,7 @@ def test_partial_then_combine_equals_fused():
 # ------------------------------------------------------------------ balanced partition
 
 def balanced_pieces(lens, groups=256):
-    """The documented num_splits = 0 cut: T pages in sequence order, G = min(256, T)
+    """The documented num_splits = 0 cut: T pages in sequence order, G = min(groups, T)
     shares, share w = pages [w T / G, (w + 1) T / G); returns {slot: (b, first page,
     end page)} and per-sequence (first slot, count)."""
     n = [(int(L) + 63) // 64 for L in lens]
@@ -288,7 +288,9 @@ def test_balanced_partition_pieces(fmt, lens, heads):
     mla.mla_decode_combine(fmt, B, H, 0, ws, out, lse)
     torch.cuda.synchronize()
     o_part, l_part, meta = (t.cpu().numpy() for t in mla.balanced_workspace_views(fmt, ws, B, H))
-    pieces, want_meta = balanced_pieces(lens)
+    groups = mla.mla_decode_partial_slots(fmt, B, H, 0) - B   # 512 where two workgroups share a unit
+    assert groups == (512 if fmt != "BF16" and H <= 32 else 256)
+    pieces, want_meta = balanced_pieces(lens, groups)
     assert np.array_equal(meta, want_meta)
     for slot, (b, p0, p1) in sorted(pieces.items()):
         ro, rl = oracle.decode(OFMT[fmt], q[b:b + 1], host, npages, bt[b:b + 1], lens[b:b + 1], SCALE,
