@@ -648,60 +648,66 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
         if (i + 4 < NK) kv[i & 3] = *(const bf16x8*)(arow + 16 * (i + 4));
       }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- sum the group's C parts in part order
+      // ---- reduce-scatter of the partial logits: wavefront `part` adds the C
+      //      parts (in part order) for regs 4 part .. 4 part + 3 only, i.e. tokens
+      //      8 part + 4 hi + [0, 4) of its lane's head, and computes their weights
+      float* xch = (float*)next;  // [wave][4][lane][4] floats
       {
-        float* xch = (float*)next;  // [wave][4][lane][4] floats
         float* xw = xch + wave * kXchFloats + 4 * lane;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) *(f32x4*)(xw + 256 * j4) = (f32x4){s[4 * j4], s[4 * j4 + 1], s[4 * j4 + 2], s[4 * j4 + 3]};
-        __syncthreads();
-        const float* xg = xch + group * C * kXchFloats + 4 * lane;
+      }
+      __syncthreads();
+      const float* xg = xch + group * C * kXchFloats + 4 * lane;
+      f32x4 sq = *(const f32x4*)(xg + 256 * part);
+#pragma unroll
+      for (int p = 1; p < C; ++p) sq += *(const f32x4*)(xg + p * kXchFloats + 256 * part);
+      if (k == k0 && !fixed) {  // a pass's reference: the first tile's max over all its tokens
+        float smax = -INFINITY;
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
           f32x4 v = *(const f32x4*)(xg + 256 * j4);
 #pragma unroll
           for (int p = 1; p < C; ++p) v += *(const f32x4*)(xg + p * kXchFloats + 256 * j4);
-          s[4 * j4] = v[0];
-          s[4 * j4 + 1] = v[1];
-          s[4 * j4 + 2] = v[2];
-          s[4 * j4 + 3] = v[3];
+          if ((k + 1) * kTileTok > limit_min) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (8 * j4 + 4 * hi + i >= limit - k * kTileTok) v[i] = -INFINITY;
+          }
+          smax = fmaxf(smax, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
         }
-        __syncthreads();  // every wavefront has read the exchange before the dequantization writes over it
-      }
-      // ---- softmax weights, as in split_pass
-      if ((k + 1) * kTileTok > limit_min) {
-        const int lt = limit - k * kTileTok;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + 4 * hi + (r & 3) >= lt) s[r] = -INFINITY;
-      }
-      if (k == k0 && !fixed) {
-        float smax = s[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
         acc.m_ref = finite_ref(fmaxf(smax, wave_partner(smax)) * a.scale_log2 + kRefLift);
       }
-      const float neg_ref = -acc.m_ref;
-      float ps = 0.0f;
-      unsigned phi[8], plo[8];
+      if ((k + 1) * kTileTok > limit_min) {  // the last tokens: the row's limit (and the sequence end)
+        const int lt = limit - k * kTileTok;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, neg_ref));
-        const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.scale_log2, neg_ref));
-        ps += pa + pb;
-        const unsigned h2 = pack_bf16x2(pa, pb);
-        phi[r >> 1] = h2;
-        plo[r >> 1] = pack_bf16x2(pa - bf16_lo(h2), pb - bf16_hi(h2));
+        for (int i = 0; i < 4; ++i)
+          if (8 * part + 4 * hi + i >= lt) sq[i] = -INFINITY;
       }
-      {
-        float smax = s[0];
+      const float neg_ref = -acc.m_ref;
+      float pw[4];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) smax = fmaxf(smax, s[r]);
+      for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[i], a.scale_log2, neg_ref));
+      acc.l_sum += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+      {
+        const float smax = fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3]));
         const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
         acc.m_seen = fmaxf(acc.m_seen, mt);
         lifted |= mt - acc.m_ref > kMaxLift;
       }
-      acc.l_sum += ps;
+      // publish the weights as the P.V operand: bp[kk][h] of a lane holds regs
+      // 8 kk .. 8 kk + 7 of that lane, so this quarter is its slots
+      // 4 (part & 1) .. + 3 of k-step part / 2 (hi and lo halves)
+      unsigned char* pbuf = (unsigned char*)(smem + 2 * kTile);  // [kk][h][lane][8 bf16]
+      {
+        const unsigned h01 = pack_bf16x2(pw[0], pw[1]), h23 = pack_bf16x2(pw[2], pw[3]);
+        const unsigned l01 = pack_bf16x2(pw[0] - bf16_lo(h01), pw[1] - bf16_hi(h01));
+        const unsigned l23 = pack_bf16x2(pw[2] - bf16_lo(h23), pw[3] - bf16_hi(h23));
+        const int kk = part >> 1, off = 8 * (part & 1) + 16 * lane;
+        *(u32x2*)(pbuf + (2 * kk) * 1024 + off) = (u32x2){h01, h23};
+        *(u32x2*)(pbuf + (2 * kk + 1) * 1024 + off) = (u32x2){l01, l23};
+      }
+      __syncthreads();  // weights published; every wavefront is past its exchange reads
       // ---- O^T (this part's channels) += khat^T . P, next tile's dequant between the MFMAs
       const int nvalid_next = min(kTileTok, L - (k + 1) * kTileTok);
       constexpr int kSub = Fill<F>::kSubsteps;
@@ -710,10 +716,9 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       constexpr int kFirst = kSlots - (kSub + kPer - 1) / kPer;     // first slot that carries steps
       bf16x8 bp[2][2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bp[kk][0] = __builtin_bit_cast(bf16x8, (u32x4){phi[4 * kk], phi[4 * kk + 1], phi[4 * kk + 2], phi[4 * kk + 3]});
-        bp[kk][1] = __builtin_bit_cast(bf16x8, (u32x4){plo[4 * kk], plo[4 * kk + 1], plo[4 * kk + 2], plo[4 * kk + 3]});
-      }
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bp[kk][h] = *(const bf16x8*)(pbuf + (2 * kk + h) * 1024 + 16 * lane);
       const __bf16* vbase = tile + tr_row0 * kRow + 8 * tr_chunk + tr_half + 32 * (part * NCT);
       auto tr_read = [&](int step) {  // step = NCT kk + ct (ct relative to this part)
         const __bf16* v0 = vbase + 16 * (step / NCT) * kRow + 32 * (step % NCT);
@@ -750,6 +755,23 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       }
       __syncthreads();
     }
+  }
+  // each wavefront summed and tracked only its quarter of every tile: combine
+  // the group's denominators (in part order, the same in every wavefront) and
+  // maxima through LDS (the tile buffers are free after the last barrier)
+  {
+    float* ex = (float*)smem;  // [wave][lane] sums, then [wave][lane] maxima
+    ex[wave * 64 + lane] = acc.l_sum;
+    ex[256 + wave * 64 + lane] = acc.m_seen;
+    __syncthreads();
+    float l = ex[group * C * 64 + lane], m = ex[256 + group * C * 64 + lane];
+#pragma unroll
+    for (int p = 1; p < C; ++p) {
+      l += ex[(group * C + p) * 64 + lane];
+      m = fmaxf(m, ex[256 + (group * C + p) * 64 + lane]);
+    }
+    acc.l_sum = l;
+    acc.m_seen = m;
   }
   return lifted;
 }
@@ -1222,10 +1244,12 @@ __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ 
 // ---------------------------------------------------------------- launchers
 
 // One head group per wavefront: two tiles and the LDS share of q, one
-// workgroup per compute unit.  Channel split: the two tiles only (the logit
-// exchange reuses the tile being refilled), two workgroups per compute unit.
+// workgroup per compute unit.  Channel split: the two tiles (the logit
+// exchange reuses the tile being refilled) and the shared weights, two
+// workgroups per compute unit (with the balanced kernel's 2112 static bytes,
+// 80960 of the 81920 bytes each may hold).
 constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
-constexpr size_t kDecodeLdsCs = 2 * (size_t)kTile * sizeof(__bf16);                 // 74752 bytes
+constexpr size_t kDecodeLdsCs = 2 * (size_t)kTile * sizeof(__bf16) + 4096;          // 78848 bytes (+ 4 KB of weights)
 template <int C> constexpr size_t decode_lds() { return C > 1 ? kDecodeLdsCs : kDecodeLds; }
 
 // The dynamic LDS size above 64 KB must be allowed once per kernel and device
