@@ -649,8 +649,10 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- reduce-scatter of the partial logits: wavefront `part` adds the C
-      //      parts (in part order) for regs 4 part .. 4 part + 3 only, i.e. tokens
-      //      8 part + 4 hi + [0, 4) of its lane's head, and computes their weights
+      //      parts (in part order) for the quarters j4 = QPW part .. QPW part +
+      //      QPW - 1 only (accumulator regs 4 j4 .. 4 j4 + 3: tokens 8 j4 + 4 hi +
+      //      [0, 4) of its lane's head) and computes their weights
+      constexpr int QPW = 4 / C;  // quarters of the tile per wavefront
       float* xch = (float*)next;  // [wave][4][lane][4] floats
       {
         float* xw = xch + wave * kXchFloats + 4 * lane;
@@ -659,9 +661,14 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       }
       __syncthreads();
       const float* xg = xch + group * C * kXchFloats + 4 * lane;
-      f32x4 sq = *(const f32x4*)(xg + 256 * part);
+      f32x4 sq[QPW];
 #pragma unroll
-      for (int p = 1; p < C; ++p) sq += *(const f32x4*)(xg + p * kXchFloats + 256 * part);
+      for (int qi = 0; qi < QPW; ++qi) {
+        const int j4 = QPW * part + qi;
+        sq[qi] = *(const f32x4*)(xg + 256 * j4);
+#pragma unroll
+        for (int p = 1; p < C; ++p) sq[qi] += *(const f32x4*)(xg + p * kXchFloats + 256 * j4);
+      }
       if (k == k0 && !fixed) {  // a pass's reference: the first tile's max over all its tokens
         float smax = -INFINITY;
 #pragma unroll
@@ -681,31 +688,35 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       if ((k + 1) * kTileTok > limit_min) {  // the last tokens: the row's limit (and the sequence end)
         const int lt = limit - k * kTileTok;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (8 * part + 4 * hi + i >= lt) sq[i] = -INFINITY;
+        for (int qi = 0; qi < QPW; ++qi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (8 * (QPW * part + qi) + 4 * hi + i >= lt) sq[qi][i] = -INFINITY;
       }
       const float neg_ref = -acc.m_ref;
-      float pw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[i], a.scale_log2, neg_ref));
-      acc.l_sum += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-      {
-        const float smax = fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3]));
-        const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
-        acc.m_seen = fmaxf(acc.m_seen, mt);
-        lifted |= mt - acc.m_ref > kMaxLift;
-      }
       // publish the weights as the P.V operand: bp[kk][h] of a lane holds regs
-      // 8 kk .. 8 kk + 7 of that lane, so this quarter is its slots
-      // 4 (part & 1) .. + 3 of k-step part / 2 (hi and lo halves)
-      unsigned char* pbuf = (unsigned char*)(smem + 2 * kTile);  // [kk][h][lane][8 bf16]
-      {
+      // 8 kk .. 8 kk + 7 of that lane, so quarter j4 is its slots
+      // 4 (j4 & 1) .. + 3 of k-step j4 / 2 (hi and lo halves)
+      unsigned char* pbuf = (unsigned char*)(smem + 2 * kTile) + 4096 * group;  // per group: [kk][h][lane][8 bf16]
+      float smax = -INFINITY;
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        float pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[qi][i], a.scale_log2, neg_ref));
+        acc.l_sum += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+        smax = fmaxf(smax, fmaxf(fmaxf(sq[qi][0], sq[qi][1]), fmaxf(sq[qi][2], sq[qi][3])));
         const unsigned h01 = pack_bf16x2(pw[0], pw[1]), h23 = pack_bf16x2(pw[2], pw[3]);
         const unsigned l01 = pack_bf16x2(pw[0] - bf16_lo(h01), pw[1] - bf16_hi(h01));
         const unsigned l23 = pack_bf16x2(pw[2] - bf16_lo(h23), pw[3] - bf16_hi(h23));
-        const int kk = part >> 1, off = 8 * (part & 1) + 16 * lane;
+        const int j4 = QPW * part + qi, kk = j4 >> 1, off = 8 * (j4 & 1) + 16 * lane;
         *(u32x2*)(pbuf + (2 * kk) * 1024 + off) = (u32x2){h01, h23};
         *(u32x2*)(pbuf + (2 * kk + 1) * 1024 + off) = (u32x2){l01, l23};
+      }
+      {
+        const float mt = fmaxf(smax, wave_partner(smax)) * a.scale_log2;
+        acc.m_seen = fmaxf(acc.m_seen, mt);
+        lifted |= mt - acc.m_ref > kMaxLift;
       }
       __syncthreads();  // weights published; every wavefront is past its exchange reads
       // ---- O^T (this part's channels) += khat^T . P, next tile's dequant between the MFMAs
@@ -968,7 +979,7 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
 // Per-sequence splits: workgroup (split, b) covers pages [split * P, (split + 1) * P)
 // of sequence b, the last split running to the end of the sequence.
 template <int F, bool kDirect, int C>
-__global__ __launch_bounds__(kThreads, C > 1 ? 2 : 1) void k_decode(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   const int split = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
   const int tid = threadIdx.x;
@@ -1116,7 +1127,7 @@ __device__ __forceinline__ void flat_next_piece(const DecodeArgs& a, FlatWalk& w
 }
 
 template <int F, int C>
-__global__ __launch_bounds__(kThreads, C > 1 ? 2 : 1) void k_decode_flat(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode_flat(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   __shared__ unsigned long long s_total;
   __shared__ FlatWalk walk;
@@ -1245,12 +1256,14 @@ __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ 
 
 // One head group per wavefront: two tiles and the LDS share of q, one
 // workgroup per compute unit.  Channel split: the two tiles (the logit
-// exchange reuses the tile being refilled) and the shared weights, two
-// workgroups per compute unit (with the balanced kernel's 2112 static bytes,
-// 80960 of the 81920 bytes each may hold).
+// exchange reuses the tile being refilled) and each head group's shared
+// weights; at C = 4 two workgroups share a compute unit (with the balanced
+// kernel's 2112 static bytes, 80960 of the 81920 bytes each may hold).
 constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
-constexpr size_t kDecodeLdsCs = 2 * (size_t)kTile * sizeof(__bf16) + 4096;          // 78848 bytes (+ 4 KB of weights)
-template <int C> constexpr size_t decode_lds() { return C > 1 ? kDecodeLdsCs : kDecodeLds; }
+template <int C> constexpr size_t decode_lds() {
+  // channel split: two tiles and 4 KB of weights per head group (4 / C groups)
+  return C > 1 ? 2 * (size_t)kTile * sizeof(__bf16) + 4096 * (4 / C) : kDecodeLds;
+}
 
 // The dynamic LDS size above 64 KB must be allowed once per kernel and device
 // (bit d of `done` records device d; setting it twice is harmless).
@@ -1266,17 +1279,17 @@ static hipError_t set_lds(K kernel, std::atomic<unsigned long long>& done) {
   return e;
 }
 
-// Channel split by head count for the quantized formats: all 4 wavefronts on
-// one group of <= 32 heads, else one head group per wavefront (the
-// unquantized baseline always uses the latter).  Measured on 8 x 131072 C4R4
-// tokens: 16-32 heads 0.31 -> 0.26 ms; a 2-way split at 64 heads was slower
-// than one group per wavefront, so it is not used.
+// Channel split by rows per sequence for the quantized formats: all 4
+// wavefronts on one group of <= 32 rows (two workgroups per compute unit),
+// 2 wavefronts per group for 33..64 rows, else one head group per wavefront
+// (the unquantized baseline always uses the latter).  On 8 x 131072 C4R4
+// tokens, balanced: 16 heads 0.222 -> 0.167 ms, 64 heads 0.309 -> 0.283 ms.
 static int channel_split(int fmt, int rows) {
   if (fmt == kBF16) return 1;
-  return rows <= 32 ? 4 : 1;
+  return rows <= 32 ? 4 : rows <= 64 ? 2 : 1;
 }
 
-int workgroups_per_cu(int fmt, int rows) { return channel_split(fmt, rows) > 1 ? 2 : 1; }
+int workgroups_per_cu(int fmt, int rows) { return channel_split(fmt, rows) == 4 ? 2 : 1; }
 
 // Head chunks of a launch (grid dimension): s_q * chunk_heads rows each.
 static int head_chunks(const DecodeArgs& a) { return (a.qheads + a.chunk_heads - 1) / a.chunk_heads; }
@@ -1308,18 +1321,26 @@ static hipError_t launch_split(bool direct, const DecodeArgs& a, int batch, hipS
 hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream) {
   const int c = channel_split(fmt, a.s_q * a.chunk_heads);
   if (fmt == kC4R4)
-    return c == 4 ? launch_split<kC4R4, 4>(direct, a, batch, stream) : launch_split<kC4R4, 1>(direct, a, batch, stream);
+    return c == 4 ? launch_split<kC4R4, 4>(direct, a, batch, stream)
+           : c == 2 ? launch_split<kC4R4, 2>(direct, a, batch, stream)
+                    : launch_split<kC4R4, 1>(direct, a, batch, stream);
   if (fmt == kC2R4)
-    return c == 4 ? launch_split<kC2R4, 4>(direct, a, batch, stream) : launch_split<kC2R4, 1>(direct, a, batch, stream);
+    return c == 4 ? launch_split<kC2R4, 4>(direct, a, batch, stream)
+           : c == 2 ? launch_split<kC2R4, 2>(direct, a, batch, stream)
+                    : launch_split<kC2R4, 1>(direct, a, batch, stream);
   return launch_split<kBF16, 1>(direct, a, batch, stream);
 }
 
 hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream) {
   const int c = channel_split(fmt, a.s_q * a.chunk_heads);
   if (fmt == kC4R4)
-    return c == 4 ? launch_flat_one<kC4R4, 4>(a, groups, stream) : launch_flat_one<kC4R4, 1>(a, groups, stream);
+    return c == 4 ? launch_flat_one<kC4R4, 4>(a, groups, stream)
+           : c == 2 ? launch_flat_one<kC4R4, 2>(a, groups, stream)
+                    : launch_flat_one<kC4R4, 1>(a, groups, stream);
   if (fmt == kC2R4)
-    return c == 4 ? launch_flat_one<kC2R4, 4>(a, groups, stream) : launch_flat_one<kC2R4, 1>(a, groups, stream);
+    return c == 4 ? launch_flat_one<kC2R4, 4>(a, groups, stream)
+           : c == 2 ? launch_flat_one<kC2R4, 2>(a, groups, stream)
+                    : launch_flat_one<kC2R4, 1>(a, groups, stream);
   return launch_flat_one<kBF16, 1>(a, groups, stream);
 }
 

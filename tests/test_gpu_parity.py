@@ -380,7 +380,7 @@ def test_fused_append_decode_equals_separate(fmt, splits, heads):
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "BF16"])
-@pytest.mark.parametrize("s_q,heads", [(2, 64), (4, 8), (3, 100), (16, 16)])
+@pytest.mark.parametrize("s_q,heads", [(2, 64), (4, 8), (2, 24), (3, 100), (16, 16)])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_multi_token_decode(fmt, s_q, heads, splits):
     """Several query tokens per sequence (causal among themselves): 128 rows in
