@@ -1178,67 +1178,84 @@ __global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode_flat(const 
 }
 
 // ---------------------------------------------------------------- combine kernels
-// One wavefront per (sequence, head): lane owns channels [8 lane, 8 lane + 8).
-// out = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse); empty splits
-// (lse = -inf) carry no weight and their partial rows are never read.
+// Two wavefronts per (sequence, head), one per half of the 512 channels: lane
+// owns channels 256 half + [4 lane, 4 lane + 4).  out = sum_s w_s o_s /
+// sum_s w_s, w_s = exp(lse_s - max lse).  The weights are computed with one
+// slot per lane (wavefront max and sum) and kept in LDS; the rows of eight
+// slots are then in flight at a time, and rows of zero weight (empty pieces,
+// lse = -inf, whose rows may hold anything) are never read.
+constexpr int kCombineMaxSlots = 512;  // slots of one sequence: <= 64 splits or <= 512 balanced shares
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
 __device__ __forceinline__ void combine_rows(const float* __restrict__ o_part, const float* __restrict__ lse_part,
-                                             int64_t first, int count, int64_t stride_rows, int64_t b, int H, int head,
-                                             __bf16* __restrict__ out, float* __restrict__ lse_out) {
+                                             int64_t first, int count, int64_t b, int H, int head, int half,
+                                             float* __restrict__ wbuf, __bf16* __restrict__ out,
+                                             float* __restrict__ lse_out) {
   const int lane = threadIdx.x & 63;
-  float M = -INFINITY;
-  for (int s = 0; s < count; ++s) M = fmaxf(M, lse_part[(first + s * stride_rows) * H + head]);
-  f32x4 acc0 = {}, acc1 = {};
+  // a sequence has at most kCombineMaxSlots pieces; the clamp only keeps LDS
+  // accesses in bounds for a workspace the decode did not write
+  count = count < kCombineMaxSlots ? count : kCombineMaxSlots;
+  // slot s's log-sum-exp in lane s % 64; the first 64 stay in a register
+  const float ls0 = lane < count ? lse_part[(first + lane) * H + head] : -INFINITY;
+  float M = ls0;
+  for (int c0 = 64; c0 < count; c0 += 64) {
+    const int s = c0 + lane;
+    M = fmaxf(M, s < count ? lse_part[(first + s) * H + head] : -INFINITY);
+  }
+  M = wave_max(M);
   float W = 0.0f;
   if (M != -INFINITY) {
-    // four slots' rows in flight at a time; rows of empty pieces (lse = -inf)
-    // are never read (they may hold anything)
-    for (int s0 = 0; s0 < count; s0 += 4) {
-      f32x4 x0[4], x1[4];
-      float wgt[4];
-      bool use[4];
-      int64_t rows[4];
+    for (int c0 = 0; c0 < count; c0 += 64) {
+      const int s = c0 + lane;
+      const float ls = c0 == 0 ? ls0 : (s < count ? lse_part[(first + s) * H + head] : -INFINITY);
+      const float w = s < count ? expf(ls - M) : 0.0f;
+      if (s < count) wbuf[s] = w;
+      W += w;
+    }
+    W = wave_sum(W);
+  }
+  f32x4 acc = {};
+  if (M != -INFINITY) {
+    const float* base = o_part + (first * H + head) * kDc + 256 * half + 4 * lane;
+    for (int s0 = 0; s0 < count; s0 += 8) {
+      float w[8];
+      f32x4 x[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = s0 + j;
-        rows[j] = (first + s * stride_rows) * H + head;
-        const float ls = s < count ? lse_part[rows[j]] : -INFINITY;
-        use[j] = ls != -INFINITY;
-        wgt[j] = use[j] ? expf(ls - M) : 0.0f;
+      for (int j = 0; j < 8; ++j) {
+        w[j] = s0 + j < count ? wbuf[s0 + j] : 0.0f;  // same address in every lane: a broadcast read
+        x[j] = (f32x4){};
+        if (w[j] > 0.0f) x[j] = *(const f32x4*)(base + (int64_t)(s0 + j) * H * kDc);  // uniform
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x0[j] = x1[j] = (f32x4){};
-        if (use[j]) {  // uniform over the wavefront
-          const float* src = o_part + rows[j] * kDc + 8 * lane;
-          x0[j] = *(const f32x4*)src;
-          x1[j] = *(const f32x4*)(src + 4);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (use[j]) {
-          W += wgt[j];
-          acc0 += wgt[j] * x0[j];
-          acc1 += wgt[j] * x1[j];
-        }
+      for (int j = 0; j < 8; ++j) acc += w[j] * x[j];
     }
   }
   const float inv = (M != -INFINITY) ? 1.0f / W : 0.0f;
-  acc0 *= inv;
-  acc1 *= inv;
-  const u32x4 packed = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
-                        pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
-  *(u32x4*)(out + (b * H + head) * kDc + 8 * lane) = packed;
-  if (lse_out && lane == 0) lse_out[b * H + head] = (M != -INFINITY) ? M + logf(W) : -INFINITY;
+  acc *= inv;
+  const u32x2 packed = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  *(u32x2*)(out + (b * H + head) * kDc + 256 * half + 4 * lane) = packed;
+  if (lse_out && half == 0 && lane == 0) lse_out[b * H + head] = (M != -INFINITY) ? M + logf(W) : -INFINITY;
 }
 
 // per-sequence splits: rows (b * S + s) * H + head
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_part, const float* __restrict__ lse_part,
                                                  int H, int S, __bf16* __restrict__ out, float* __restrict__ lse_out) {
-  const int b = blockIdx.y;
-  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float wbuf[4][kCombineMaxSlots];
+  const int b = blockIdx.y, wave = threadIdx.x >> 6;
+  const int head = blockIdx.x * 2 + (wave >> 1);
   if (head >= H) return;
-  combine_rows(o_part, lse_part, (int64_t)b * S, S, 1, b, H, head, out, lse_out);
+  combine_rows(o_part, lse_part, (int64_t)b * S, S, b, H, head, wave & 1, wbuf[wave], out, lse_out);
 }
 
 // balanced partition: slots [meta[2b], meta[2b] + meta[2b + 1]) of sequence b
@@ -1246,10 +1263,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_par
 __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, const int* __restrict__ meta,
                                                       int H, __bf16* __restrict__ out, float* __restrict__ lse_out) {
-  const int b = blockIdx.y;
-  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float wbuf[4][kCombineMaxSlots];
+  const int b = blockIdx.y, wave = threadIdx.x >> 6;
+  const int head = blockIdx.x * 2 + (wave >> 1);
   if (head >= H) return;
-  combine_rows(o_part, lse_part, meta[2 * b], meta[2 * b + 1], 1, b, H, head, out, lse_out);
+  combine_rows(o_part, lse_part, meta[2 * b], meta[2 * b + 1], b, H, head, wave & 1, wbuf[wave], out, lse_out);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1346,14 +1364,14 @@ hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStrea
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int batch, int heads, int splits,
                           __bf16* out, float* lse_out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_combine, dim3((heads + 3) / 4, batch), dim3(256), 0, stream, o_part, lse_part, heads, splits,
+  hipLaunchKernelGGL(k_combine, dim3((heads + 1) / 2, batch), dim3(256), 0, stream, o_part, lse_part, heads, splits,
                      out, lse_out);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_flat(const float* o_part, const float* lse_part, const int* meta, int batch, int heads,
                                __bf16* out, float* lse_out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_combine_flat, dim3((heads + 3) / 4, batch), dim3(256), 0, stream, o_part, lse_part, meta,
+  hipLaunchKernelGGL(k_combine_flat, dim3((heads + 1) / 2, batch), dim3(256), 0, stream, o_part, lse_part, meta,
                      heads, out, lse_out);
   return hipGetLastError();
 }
