@@ -8,9 +8,11 @@
 //
 // One workgroup = one piece of work (a page range of one sequence: a fixed
 // split, or a share of the balanced partition), 256 threads = 4 wavefronts,
-// one per SIMD.  Wave w owns heads [32w, 32w + 32) (for <= 32 heads the four
-// wavefronts split the channels of one head group instead, see
-// split_pass_cs).  The work is tiled by half pages (32 tokens):
+// one per SIMD.  Wave w owns heads [32w, 32w + 32); at <= 64 rows per
+// sequence the wavefronts of a head group split its channels instead (four
+// per group at <= 32 rows, two workgroups per compute unit; two per group at
+// 33..64 rows), sharing one softmax through LDS, see split_pass_cs.  The work
+// is tiled by half pages (32 tokens):
 //   1. fill: every thread loads its share of the next tile's packed bytes
 //      (16-byte loads; the 32 lanes of a half-wave read 512 contiguous bytes of
 //      one code chunk), dequantizes them in registers once for all heads
@@ -28,7 +30,8 @@
 //      is recomputed with its true max (see split_pass).
 //   4. P.V on MFMA 32x32x16 bf16 with the latent as value: A = khat^T read
 //      with ds_read_b64_tr_b16 (transposing 16-bit loads) from the same tile,
-//      B = P straight from the softmax registers.  P is split into a bf16 high
+//      B = P straight from the softmax registers (through LDS where the
+//      channels are split).  P is split into a bf16 high
 //      part and a bf16 remainder (two MFMAs sharing A) so the weights keep
 //      ~16 significant bits; a single bf16 P loses too much accuracy when a few
 //      tokens with large, cancelling latent values dominate a head.
@@ -568,17 +571,21 @@ __device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16
 }
 
 // ---------------------------------------------------------------- channel-split variant
-// For num_heads <= 32 one head group per wavefront would leave three
-// wavefronts (SIMDs) without MFMA work, and one tile in flight per compute
-// unit keeps HBM far from busy.  Here the 4 wavefronts form 4 / C head groups
-// of C wavefronts (the launcher uses C = 4 for <= 32 heads); part c of a group takes
+// For <= 64 rows per sequence one head group per wavefront would leave two or
+// three wavefronts (SIMDs) without MFMA work, and one tile in flight per
+// compute unit keeps HBM far from busy.  Here the 4 wavefronts form 4 / C head
+// groups of C wavefronts (the launcher uses C = 4 for <= 32 rows, C = 2 for
+// 33..64); part c of a group takes
 // k-steps [c NK, (c + 1) NK) of Q.K^T (NK = 36 / C, q entirely in registers)
 // and channels [c 512 / C, (c + 1) 512 / C) of P.V (O in 256 / C
-// accumulators).  The partial logits go through LDS; every wavefront of the
-// group adds the C parts in the same order, so all of them hold bitwise the
-// same S, weights and denominator.  The packed bytes of the next D tiles are
-// kept in registers; with two workgroups per compute unit (the launch bound
-// below) D = 1: the other workgroup's work covers the load latency.
+// accumulators).  The partial logits go through LDS as a reduce-scatter:
+// wavefront c adds the C parts (in part order) for its 4 / C quarters of the
+// tile only, computes their weights and publishes them as the P.V operand in
+// LDS, which every wavefront of the group then reads; the denominators and
+// maxima of the quarters are combined at the end of the pass, so all
+// wavefronts of a group hold bitwise the same weights and denominator.  The
+// packed bytes of the next D tiles are kept in registers (D = 1: at C = 4 the
+// other workgroup on the compute unit covers the load latency).
 template <int C> struct CsAcc {
   f32x16 o[16 / C];
   float l_sum, m_ref, m_seen;
@@ -596,9 +603,9 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
   const int part = wave % C, group = wave / C;
   // the partial logits go through the tile buffer that receives the next
   // tile: it is free from the end of the previous P.V until this tile's
-  // dequantization starts (after the barrier that follows the exchange), so
-  // the pass needs only the two tile buffers and two workgroups fit on a
-  // compute unit
+  // dequantization starts (after the barrier that follows the weights), so
+  // the pass needs only the two tile buffers and the weights blocks, and at
+  // C = 4 two workgroups fit on a compute unit
   const int g = lane >> 4, i16 = lane & 15;
   const int tr_row0 = 4 * (i16 >> 2) + (g >> 1);
   const int tr_chunk = 2 * (g & 1) + ((i16 & 3) >> 1);
