@@ -70,11 +70,19 @@ KERNEL_SOURCES = ("bit_mla_kv_decode_amd/csrc/decode.hip", "bit_mla_kv_decode_am
 
 
 def kernel_source_sha256():
+    """SHA-256 of the decode kernel's sources with comments, blank lines and
+    trailing spaces removed: edits to comments keep the counted traffic valid,
+    any change to the code drops it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            txt = f.read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", "", txt)
+        lines = [l.rstrip() for l in txt.split("\n")]
+        h.update("\n".join(l for l in lines if l).encode())
     return h.hexdigest()
 
 

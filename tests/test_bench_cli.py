@@ -45,3 +45,22 @@ def test_traffic_gate_follows_the_kernel_sources(tmp_path, monkeypatch):
     f.write_text("kernel_source_sha256: %s\ntraffic_bytes_per_launch: 1234\n" % ("0" * 64))
     assert bench.counted_traffic("demo", "C4R4") is None
     assert bench.counted_traffic("missing", "C4R4") is None
+
+
+def test_kernel_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    import bench
+    def tree(code):
+        root = tmp_path / ("t%d" % len(list(tmp_path.iterdir())))
+        for rel in bench.KERNEL_SOURCES:
+            f = root / rel
+            f.parent.mkdir(parents=True, exist_ok=True)
+            f.write_text(code)
+        return str(root)
+    base = "int f(int x) {\n  return x + 1;\n}\n"
+    commented = "// header comment\nint f(int x) {  /* inline\n block */\n\n  return x + 1;  // trailing\n}\n"
+    changed = "int f(int x) {\n  return x + 2;\n}\n"
+    hashes = []
+    for code in (base, commented, changed):
+        monkeypatch.setattr(bench, "ROOT", tree(code))
+        hashes.append(bench.kernel_source_sha256())
+    assert hashes[0] == hashes[1] != hashes[2]
