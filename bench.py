@@ -272,7 +272,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "format": w.fmt, "batch": B, "heads": H, "ctx": max_len,
                    "tokens": tokens, "page_size": 64, "cache_replicas": replicas,
-                   "partition": "balanced (256 equal page shares)" if S == 0 else "%d splits per sequence" % S,
+                   "partition": ("balanced (%d equal page shares)" % (mla.mla_decode_partial_slots(w.fmt, B, H, 0) - B)
+                                 if S == 0 else "%d splits per sequence" % S),
                    "step": ("quant_append(1 token/seq) + split-KV decode + LSE combine" if args.unfused else
                             "fused append(1 token/seq) + split-KV decode, then LSE combine"),
                    "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
