@@ -156,12 +156,15 @@ def test_empty_sequences(splits):
     assert_lse(lse, ref_lse)
 
 
+@pytest.mark.parametrize("heads", [128, 48, 16])
 @pytest.mark.parametrize("qmax", [40.0, 11.0])
-def test_large_logit_jump(qmax):
+def test_large_logit_jump(qmax, heads):
     """Logits that rise far above the first tile's after it: with qmax = 40 the
     rise (up to ~250 in log2 units) exceeds the kernel's fixed-reference range
     and the split is recomputed; with qmax = 11 (rises up to ~70-110) it stays
-    inside the range.  Both must give the exact softmax."""
+    inside the range.  Both must give the exact softmax, with one head group
+    per wavefront (128 heads), two wavefronts per group (48) and four (16)."""
+    _say("logit jump qmax=%g H=%d" % (qmax, heads))
     fmt = "C4R4"
     L = 300
     g = torch.Generator().manual_seed(5)
@@ -170,8 +173,8 @@ def test_large_logit_jump(qmax):
     lat[250, 7] = -40.0
     lat = lat.to(torch.bfloat16)
     rope = torch.randn(L, 64, generator=g).to(torch.bfloat16)
-    q = torch.randn(1, 128, 576, generator=g)
-    q[0, :, 0] = qmax * torch.rand(128, generator=g)
+    q = torch.randn(1, heads, 576, generator=g)
+    q[0, :, 0] = qmax * torch.rand(heads, generator=g)
     q = q.to(torch.bfloat16)
     bt = np.arange(5, dtype=np.int32)[None]
     lens = np.array([L], np.int32)
