@@ -685,9 +685,10 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
 #pragma unroll
           for (int p = 1; p < C; ++p) v += *(const f32x4*)(xg + p * kXchFloats + 256 * j4);
           if ((k + 1) * kTileTok > limit_min) {
+            const int lt = limit - k * kTileTok, lt_l = lt - 4 * hi;  // see the masking of the quarters below
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (8 * j4 + 4 * hi + i >= limit - k * kTileTok) v[i] = -INFINITY;
+              if (C == 4 ? 8 * j4 + i >= lt_l : 8 * j4 + 4 * hi + i >= lt) v[i] = -INFINITY;
           }
           smax = fmaxf(smax, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
         }
@@ -695,11 +696,15 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       }
       if ((k + 1) * kTileTok > limit_min) {  // the last tokens: the row's limit (and the sequence end)
         const int lt = limit - k * kTileTok;
+        // at C = 4 (256 registers per wavefront) per-lane token indices would
+        // be hoisted out of the loop and spilled: compare one per-lane bound
+        // against compile-time offsets there
+        const int lt_l = lt - 4 * hi - 8 * QPW * part;
 #pragma unroll
         for (int qi = 0; qi < QPW; ++qi)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (8 * (QPW * part + qi) + 4 * hi + i >= lt) sq[qi][i] = -INFINITY;
+            if (C == 4 ? 8 * qi + i >= lt_l : 8 * (QPW * part + qi) + 4 * hi + i >= lt) sq[qi][i] = -INFINITY;
       }
       const float neg_ref = -acc.m_ref;
       // publish the weights as the P.V operand: bp[kk][h] of a lane holds regs
