@@ -8,6 +8,7 @@
 namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -97,10 +98,11 @@ __global__ __launch_bounds__(256) void k_mfma_cycles(int iters, unsigned long lo
 }
 
 // LDS bandwidth: each workgroup holds 64 KiB of LDS (at most two per compute
-// unit); thread t reads (or writes) 16 bytes at t * 16 + 4096 j + 16 (i & 1),
-// j < 8 (no bank conflicts, all inside the first 40 KiB), `iters` times.
-// Thread 0 stores the s_memtime delta of the loop.
-template <bool WRITE>
+// unit); thread t reads (or writes) W bytes (W = 4, 8 or 16) at t W + 4096 j
+// + 16 (i & 1), j < 8 (consecutive lanes on consecutive words: no bank
+// conflicts; all inside the first 45 KiB), `iters` times.  Thread 0 stores
+// the s_memtime delta of the loop.
+template <int W, bool WRITE>
 __global__ __launch_bounds__(512) void k_lds(int iters, unsigned long long* __restrict__ cycles,
                                              unsigned* __restrict__ sink) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[65536];
@@ -112,9 +114,21 @@ __global__ __launch_bounds__(512) void k_lds(int iters, unsigned long long* __re
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      unsigned char* p = lds + t * 16 + j * 4096 + 16 * (it & 1);
-      if (WRITE) *(u32x4*)p = acc + (u32x4){(unsigned)it, 0u, 0u, 0u};
-      else acc ^= *(const u32x4*)p;
+      unsigned char* p = lds + t * W + j * 4096 + 16 * (it & 1);
+      if (WRITE) {
+        const u32x4 v = acc + (u32x4){(unsigned)it, 0u, 0u, 0u};
+        if (W == 4) *(unsigned*)p = v.x;
+        if (W == 8) *(u32x2*)p = (u32x2){v.x, v.y};
+        if (W == 16) *(u32x4*)p = v;
+      } else {
+        if (W == 4) acc.x ^= *(const unsigned*)p;
+        if (W == 8) {
+          const u32x2 r = *(const u32x2*)p;
+          acc.x ^= r.x;
+          acc.y ^= r.y;
+        }
+        if (W == 16) acc ^= *(const u32x4*)p;
+      }
     }
     asm volatile("" ::"v"(lds) : "memory");  // the array escapes: every store stays
   }
@@ -123,6 +137,16 @@ __global__ __launch_bounds__(512) void k_lds(int iters, unsigned long long* __re
   if (t == 0) cycles[blockIdx.x] = t1 - t0;
   acc ^= *(const u32x4*)(lds + 16 * ((t + 1) % blockDim.x));
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x12345678u) sink[(int64_t)blockIdx.x * blockDim.x + t] = acc.x;
+}
+
+template <int W>
+hipError_t launch_lds(bool write, int groups, dim3 block, int iters, unsigned long long* cycles, unsigned* sink,
+                      hipStream_t st) {
+  if (write)
+    hipLaunchKernelGGL((k_lds<W, true>), dim3(groups), block, 0, st, iters, cycles, sink);
+  else
+    hipLaunchKernelGGL((k_lds<W, false>), dim3(groups), block, 0, st, iters, cycles, sink);
+  return hipGetLastError();
 }
 
 template <int CH>
@@ -183,16 +207,18 @@ int32_t peak_mfma_cycles(int32_t groups, int32_t iters, int32_t chains, int32_t 
   return status(e);
 }
 
-int32_t peak_lds(int32_t groups, int32_t waves_per_simd, int32_t write, int32_t iters, uint64_t* cycles,
-                 uint32_t* sink, void* stream) {
-  if (!cycles || !sink || groups < 1 || iters < 0 || (waves_per_simd != 1 && waves_per_simd != 2))
+int32_t peak_lds(int32_t groups, int32_t waves_per_simd, int32_t write, int32_t width, int32_t iters,
+                 uint64_t* cycles, uint32_t* sink, void* stream) {
+  if (!cycles || !sink || groups < 1 || iters < 0 || (waves_per_simd != 1 && waves_per_simd != 2) ||
+      (width != 4 && width != 8 && width != 16))
     return (int32_t)hipErrorInvalidValue;
   const dim3 block(256 * waves_per_simd);
-  if (write)
-    hipLaunchKernelGGL(k_lds<true>, dim3(groups), block, 0, (hipStream_t)stream, iters, (unsigned long long*)cycles, sink);
-  else
-    hipLaunchKernelGGL(k_lds<false>, dim3(groups), block, 0, (hipStream_t)stream, iters, (unsigned long long*)cycles, sink);
-  return status(hipGetLastError());
+  unsigned long long* c = (unsigned long long*)cycles;
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = width == 4   ? launch_lds<4>(write != 0, groups, block, iters, c, sink, st)
+                       : width == 8 ? launch_lds<8>(write != 0, groups, block, iters, c, sink, st)
+                                    : launch_lds<16>(write != 0, groups, block, iters, c, sink, st);
+  return status(e);
 }
 
 }  // extern "C"

@@ -187,13 +187,14 @@ def section_peaks():
                   "cycles_per_mfma": round(per, 1), "shader_clock_GHz": round(ghz, 2)})
     lsink = torch.zeros(G * 512, dtype=torch.int32, device="cuda")
     for write in (False, True):
-        for waves in (1, 2):
-            peaks.lds(G, waves, write, 20000, cyc, lsink, st)
-            by = peaks.lds(G, waves, write, 20000, cyc, lsink, st)
-            torch.cuda.synchronize()
-            c = float(np.median(cyc[:G].double().cpu().numpy()))
-            emit({"row": "lds_bandwidth", "op": "write_b128" if write else "read_b128", "waves_per_simd": waves,
-                  "bytes_per_cycle_per_cu": round(by / c, 1)})
+        for width in (4, 8, 16):
+            for waves in (1, 2):
+                peaks.lds(G, waves, write, 20000, cyc, lsink, st, width=width)
+                by = peaks.lds(G, waves, write, 20000, cyc, lsink, st, width=width)
+                torch.cuda.synchronize()
+                c = float(np.median(cyc[:G].double().cpu().numpy()))
+                emit({"row": "lds_bandwidth", "op": ("write_b%d" if write else "read_b%d") % (8 * width),
+                      "waves_per_simd": waves, "bytes_per_cycle_per_cu": round(by / c, 1)})
 
 
 def section_configs():

@@ -22,7 +22,7 @@ def load_library():
         L.peak_read.argtypes, L.peak_read.restype = [vp, sz, i32, vp, vp], i32
         L.peak_mfma_bf16.argtypes, L.peak_mfma_bf16.restype = [i32, i32, vp, vp], i32
         L.peak_mfma_cycles.argtypes, L.peak_mfma_cycles.restype = [i32, i32, i32, i32, vp, vp, vp], i32
-        L.peak_lds.argtypes, L.peak_lds.restype = [i32, i32, i32, i32, vp, vp, vp], i32
+        L.peak_lds.argtypes, L.peak_lds.restype = [i32, i32, i32, i32, i32, vp, vp, vp], i32
         _lib = L
     return _lib
 
@@ -63,11 +63,11 @@ def mfma_cycles(groups, iters, chains, valu_per_mfma, cycles, sink, stream=None)
                                         _s(stream)), "peak_mfma_cycles")
 
 
-def lds(groups, waves_per_simd, write, iters, cycles, sink, stream=None):
-    """LDS read (write=False) or write bandwidth loop; cycles (int64 device tensor
-    of groups) receives each workgroup's shader-clock cycles.  Returns the
-    bytes one workgroup moves."""
+def lds(groups, waves_per_simd, write, iters, cycles, sink, stream=None, width=16):
+    """LDS read (write=False) or write bandwidth loop with `width`-byte accesses
+    (4, 8 or 16); cycles (int64 device tensor of groups) receives each
+    workgroup's shader-clock cycles.  Returns the bytes one workgroup moves."""
     assert cycles.numel() >= groups and sink.numel() >= groups * 256 * waves_per_simd
-    _ck(load_library().peak_lds(groups, waves_per_simd, int(write), iters, cycles.data_ptr(), sink.data_ptr(),
-                                _s(stream)), "peak_lds")
-    return iters * 8 * 16 * 256 * waves_per_simd
+    _ck(load_library().peak_lds(groups, waves_per_simd, int(write), width, iters, cycles.data_ptr(),
+                                sink.data_ptr(), _s(stream)), "peak_lds")
+    return iters * 8 * width * 256 * waves_per_simd

@@ -45,13 +45,15 @@ int32_t peak_mfma_cycles(int32_t groups, int32_t iters, int32_t chains, int32_t 
 
 /* LDS bandwidth: `groups` workgroups of 256 * waves_per_simd threads (1 or 2
  * wavefronts per SIMD), each holding 64 KiB of LDS; every thread reads
- * (write = 0) or writes (write != 0) 8 conflict-free 16-byte words per round,
- * `iters` rounds.  cycles[g] = shader-clock cycles of workgroup g's loop, so
- * bytes per cycle per compute unit = iters * 8 * 16 * threads / cycles when
- * one workgroup runs per compute unit.  sink holds groups * 256 *
- * waves_per_simd words, written only for an unlikely value. */
-int32_t peak_lds(int32_t groups, int32_t waves_per_simd, int32_t write, int32_t iters, uint64_t* cycles,
-                 uint32_t* sink, void* stream);
+ * (write = 0) or writes (write != 0) 8 conflict-free words of `width` bytes
+ * (4, 8 or 16: ds_read/ds_write _b32, _b64, _b128) per round, `iters`
+ * rounds.  cycles[g] = shader-clock cycles of workgroup g's loop, so bytes
+ * per cycle per compute unit = iters * 8 * width * threads / cycles when one
+ * workgroup runs per compute unit.  sink holds groups * 256 * waves_per_simd
+ * words, written only for an unlikely value.  Invalid arguments return
+ * hipErrorInvalidValue before any launch. */
+int32_t peak_lds(int32_t groups, int32_t waves_per_simd, int32_t write, int32_t width, int32_t iters,
+                 uint64_t* cycles, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -45,8 +45,9 @@ def test_peaks_header_symbols_are_exported():
     assert lib.peak_mfma_cycles(256, 10, 3, 0, A, A2, None) != 0     # 1 or 2 chains
     assert lib.peak_mfma_cycles(256, 10, 2, 5, A, A2, None) != 0     # 0, 2, 4, 6, 8 or 12 FMAs
     assert lib.peak_mfma_cycles(0, 10, 2, 0, A, A2, None) != 0
-    assert lib.peak_lds(256, 3, 0, 10, A, A2, None) != 0             # 1 or 2 wavefronts per SIMD
-    assert lib.peak_lds(0, 1, 0, 10, A, A2, None) != 0
+    assert lib.peak_lds(256, 3, 0, 16, 10, A, A2, None) != 0         # 1 or 2 wavefronts per SIMD
+    assert lib.peak_lds(0, 1, 0, 16, 10, A, A2, None) != 0
+    assert lib.peak_lds(256, 1, 0, 12, 10, A, A2, None) != 0         # widths 4, 8, 16 only
 
 
 def test_format_queries():
