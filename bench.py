@@ -149,6 +149,96 @@ def cpu_baseline(w, seqs=8):
                               "sample": "%d tokens of one sequence, all heads, %.2f s" % (n1, dt1)}}
 
 
+def time_case(w, args, fused, S, dev, label=None):
+    """Build `w`'s caches on the GPU and time the decode step on them: returns
+    the step time, the decode kernel's average time (HIP events on its stream),
+    packed GB/s and the kernel's roofline block."""
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    tok_bytes = mla.mla_token_bytes(w.fmt)
+    lens_all = W_seq_lens(w)
+    cache_bytes = int(((lens_all.astype(np.int64) + 63) // 64).sum()) * mla.mla_page_bytes(w.fmt)
+    replicas = max(1, min(4, math.ceil(1.0e9 / cache_bytes)))
+    log("building %s: B=%d H=%d fmt=%s, %.1f MB packed cache x %d replicas"
+        % (label or w.name, w.batch, w.heads, w.fmt, cache_bytes / 1e6, replicas))
+    lens, bt, npages, caches, q, new_lat, new_rope, new_slots = build_workload(w, dev, replicas)
+    B, H = w.batch, w.heads
+    max_len = int(lens.max())
+    ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, H, S), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    bt_d = torch.from_numpy(bt).to(dev)
+    sl_d = torch.from_numpy(lens).to(dev)
+    stream = torch.cuda.current_stream()
+    tokens = int(lens.sum())
+    packed_bytes = tokens * tok_bytes
+    flops = tokens * 2.0 * H * (576 + 512)          # algorithmic: Q.K^T over 576 + P.V over 512
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i, timed=None):
+        c = caches[i % replicas]
+        if not fused:
+            mla.mla_quant_append(w.fmt, new_lat, new_rope, new_slots, c, stream=stream)
+        if timed is not None:
+            timed[0].record(stream)
+        if fused:
+            mla.mla_decode_append_partial(w.fmt, new_lat, new_rope, q, c, bt_d, sl_d, w.softmax_scale, S, ws,
+                                          max_seq_len=max_len, stream=stream)
+        else:
+            mla.mla_decode_partial(w.fmt, q, c, bt_d, sl_d, w.softmax_scale, S, ws, max_seq_len=max_len,
+                                   stream=stream)
+        if timed is not None:
+            timed[1].record(stream)
+        mla.mla_decode_combine(w.fmt, B, H, S, ws, out, lse, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    ms_step = total * 1e3 / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = packed_bytes / (ms_step * 1e-3) / 1e9
+    k_gbs = packed_bytes / (k_ms * 1e-3) / 1e9
+    k_tflops = flops / (k_ms * 1e-3) / 1e12
+    log("%s: step %.3f ms, decode kernel %.3f ms: %.1f GB/s packed per step (%.1f%% of HBM), kernel %.1f GB/s, "
+        "%.1f TFLOP/s (%.1f%% of bf16 MFMA)" % (label or w.name, ms_step, k_ms, value, 100 * value / HBM_PEAK_GBS,
+                                             k_gbs, k_tflops, 100 * k_tflops / BF16_MFMA_PEAK_TFLOPS))
+    # the decode kernel's binding roof: MFMA when its algorithmic intensity is
+    # above the MI355X ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), else HBM
+    intensity = flops / packed_bytes
+    if intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        bound, achieved, peak, unit = "mfma", k_tflops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", k_gbs, HBM_PEAK_GBS, "GB/s"
+    roofline = {"kernel": ("k_decode_flat (balanced split-KV partial" if S == 0 else "k_decode (split-KV partial") +
+                          (", fused append)" if fused else ")"),
+                "bound": bound, "achieved": round(achieved, 2),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel_ms": round(k_ms, 4), "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
+                "intensity_flop_per_byte": round(intensity, 1),
+                "kernel_packed_gbs": round(k_gbs, 2), "kernel_hbm_peak_frac": round(k_gbs / HBM_PEAK_GBS, 4)}
+    res = {"workload": w.name, "format": w.fmt, "batch": B, "heads": H, "ctx": max_len, "tokens": tokens,
+           "cache_replicas": replicas, "ms_per_step": round(ms_step, 4), "value": round(value, 2), "unit": "GB/s",
+           "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+           "partition": ("balanced (%d equal page shares)" % (mla.mla_decode_partial_slots(w.fmt, B, H, 0) - B)
+                         if S == 0 else "%d splits per sequence" % S),
+           "roofline": roofline}
+    del caches, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def W_seq_lens(w):
+    from bit_mla_kv_decode_amd import workloads as W
+    return W.seq_lens(w)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +250,8 @@ def main():
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count (head sweep)")
     ap.add_argument("--format", default="", help="override the cache format: C4R4, C2R4 or BF16 (same data)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time the headline workload only (no C2R4 / BF16 / 16-head records)")
     ap.add_argument("--unfused", action="store_true", help="separate append launch before the decode")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -181,75 +273,33 @@ def main():
         w = W.derive(w, heads=args.heads)
     if args.format:
         w = W.derive(w, fmt=args.format)
-    tok_bytes = mla.mla_token_bytes(w.fmt)
-    lens_all = W.seq_lens(w)
-    cache_bytes = int(((lens_all.astype(np.int64) + 63) // 64).sum()) * mla.mla_page_bytes(w.fmt)
-    replicas = max(1, min(4, math.ceil(1.0e9 / cache_bytes)))
-    log("building %s: B=%d H=%d fmt=%s, %.1f MB packed cache x %d replicas"
-        % (w.name, w.batch, w.heads, w.fmt, cache_bytes / 1e6, replicas))
-    lens, bt, npages, caches, q, new_lat, new_rope, new_slots = build_workload(w, dev, replicas)
-    B, H = w.batch, w.heads
-    max_len = int(lens.max())
     S = args.splits
-    ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, B, H, S), dtype=torch.uint8, device=dev)
-    out = torch.empty(B, H, 512, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-    bt_d = torch.from_numpy(bt).to(dev)
-    sl_d = torch.from_numpy(lens).to(dev)
-    stream = torch.cuda.current_stream()
-    tokens = int(lens.sum())
-    packed_bytes = tokens * tok_bytes
-    flops = tokens * 2.0 * H * (576 + 512)          # algorithmic: Q.K^T over 576 + P.V over 512
+    head = time_case(w, args, not args.unfused, S, dev)
+    roofline = head["roofline"]
+    if S == 0 and not args.heads and not args.format and not args.unfused:
+        roofline["traffic"] = counted_traffic(w.name, w.fmt)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-
-    def step(i, timed=None):
-        c = caches[i % replicas]
-        if args.unfused:
-            mla.mla_quant_append(w.fmt, new_lat, new_rope, new_slots, c, stream=stream)
-        if timed is not None:
-            timed[0].record(stream)
-        if args.unfused:
-            mla.mla_decode_partial(w.fmt, q, c, bt_d, sl_d, w.softmax_scale, S, ws, max_seq_len=max_len,
-                                   stream=stream)
-        else:
-            mla.mla_decode_append_partial(w.fmt, new_lat, new_rope, q, c, bt_d, sl_d, w.softmax_scale, S, ws,
-                                          max_seq_len=max_len, stream=stream)
-        if timed is not None:
-            timed[1].record(stream)
-        mla.mla_decode_combine(w.fmt, B, H, S, ws, out, lse, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    total = time.perf_counter() - t0
-    ms_step = total * 1e3 / args.steps
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    value = packed_bytes / (ms_step * 1e-3) / 1e9
-    k_tflops = flops / (k_ms * 1e-3) / 1e12
-    log("step %.3f ms, decode kernel %.3f ms: %.1f GB/s packed (%.1f%% of HBM), %.1f TFLOP/s (%.1f%% of bf16 MFMA)"
-        % (ms_step, k_ms, value, 100 * value / HBM_PEAK_GBS, k_tflops, 100 * k_tflops / BF16_MFMA_PEAK_TFLOPS))
-
-    # the decode kernel's binding roof: MFMA when its algorithmic intensity is
-    # above the MI355X ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), else HBM
-    intensity = flops / packed_bytes
-    if intensity > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        bound, achieved, peak, unit = "mfma", k_tflops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
-    else:
-        bound, achieved, peak, unit = "hbm", packed_bytes / (k_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    traffic = (counted_traffic(w.name, w.fmt) if (S == 0 and not args.heads and not args.format and not args.unfused)
-               else None)
-    roofline = {"kernel": ("k_decode_flat (balanced split-KV partial" if S == 0 else "k_decode (split-KV partial") +
-                          (")" if args.unfused else ", fused append)"),
-                "bound": bound, "achieved": round(achieved, 2),
-                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel_ms": round(k_ms, 4), "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
-                "intensity_flop_per_byte": round(intensity, 1)}
+    # the other formats the metric names, each with its own roofline block:
+    # C2R4 on its 64 x 32768 workload (5% outlier channels), the unquantized
+    # BF16 cache on the same data (the in-house baseline kernel), BF16 on the
+    # headline's data, and the 16-head share of the headline cache (the
+    # HBM-bound regime of a head-sharded deployment)
+    extra = {}
+    if not args.no_extra and not args.heads and not args.format and args.workload == "c4r4_128k":
+        c2 = W.WORKLOADS["c2r4_32k_outliers"]
+        extra["c2r4_32k_outliers"] = time_case(c2, args, not args.unfused, S, dev)
+        extra["bf16_on_c2r4_32k_outliers"] = time_case(W.derive(c2, fmt="BF16"), args, not args.unfused, S, dev,
+                                                       label="bf16 cache, c2r4_32k_outliers data")
+        extra["bf16_on_c4r4_128k"] = time_case(W.derive(w, fmt="BF16"), args, not args.unfused, S, dev,
+                                               label="bf16 cache, c4r4_128k data")
+        extra["c4r4_128k_16_heads"] = time_case(W.derive(w, heads=16), args, not args.unfused, S, dev,
+                                                label="c4r4_128k, 16 heads")
+        for lo, bf in (("c2r4_32k_outliers", "bf16_on_c2r4_32k_outliers"), (None, "bf16_on_c4r4_128k")):
+            lo_ms = extra[lo]["roofline"]["kernel_ms"] if lo else roofline["kernel_ms"]
+            lo_step = extra[lo]["ms_per_step"] if lo else head["ms_per_step"]
+            extra[bf]["lowbit_speedup_kernel"] = round(extra[bf]["roofline"]["kernel_ms"] / lo_ms, 3)
+            extra[bf]["lowbit_speedup_step"] = round(extra[bf]["ms_per_step"] / lo_step, 3)
+            extra[bf]["compared_with"] = lo or w.name
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -257,29 +307,32 @@ def main():
         cpu = cpu_baseline(w)
         log("cpu baseline: %s" % cpu)
 
+    tok_bytes = mla.mla_token_bytes(w.fmt)
     rec = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "format": w.fmt, "batch": B, "heads": H, "ctx": max_len,
-                   "tokens": tokens, "page_size": 64, "cache_replicas": replicas,
-                   "partition": ("balanced (%d equal page shares)" % (mla.mla_decode_partial_slots(w.fmt, B, H, 0) - B)
-                                 if S == 0 else "%d splits per sequence" % S),
+        "config": {"workload": w.name, "format": w.fmt, "batch": head["batch"], "heads": head["heads"],
+                   "ctx": head["ctx"], "tokens": head["tokens"], "page_size": 64,
+                   "cache_replicas": head["cache_replicas"], "partition": head["partition"],
                    "step": ("quant_append(1 token/seq) + split-KV decode + LSE combine" if args.unfused else
                             "fused append(1 token/seq) + split-KV decode, then LSE combine"),
-                   "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
+                   "hbm_peak_frac": head["hbm_peak_frac"],
+                   "compression_vs_bf16": round(1152.0 / tok_bytes, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if extra:
+        rec["formats"] = extra
     print(json.dumps(rec), flush=True)
 
 

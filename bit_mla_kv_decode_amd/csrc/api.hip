@@ -3,6 +3,7 @@
 // for the contract of every entry point.
 #include "mla_lowbit.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -21,9 +22,13 @@ mla_status_t fail(mla_status_t s, const char* fmt, ...) {
   return s;
 }
 
-// Compute units of one MI355X; the split heuristic aims at whole waves of
-// one workgroup per compute unit.
-constexpr int kComputeUnits = 256;
+// Compute units the decode plans for: the current device's count (256 on an
+// MI355X), queried once per device, at most kMaxComputeUnits so that a
+// sequence never has more balanced pieces than the combine kernel merges
+// (two workgroups per unit: 512).  Without a device (host-only use of the
+// size queries) the MI355X count is assumed.
+constexpr int kMaxComputeUnits = 256;
+constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxPagesPerSplit = 128;
 // 2^24 pages = 2^30 tokens per sequence keeps every in-kernel token and
@@ -52,9 +57,24 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+int compute_units() {
+  static std::atomic<int> known[kMaxDevices];  // 0: not queried yet
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kMaxComputeUnits;
+  int n = known[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      v = kMaxComputeUnits;
+    n = v < kMaxComputeUnits ? v : kMaxComputeUnits;
+    known[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Workgroups that run at once: one per compute unit, two where the decode
 // kernel splits channels (<= 32 rows per sequence, quantized formats).
-int resident_groups(int fmt, int rows) { return kComputeUnits * mla::workgroups_per_cu(fmt, rows); }
+int resident_groups(int fmt, int rows) { return compute_units() * mla::workgroups_per_cu(fmt, rows); }
 
 // Partial-row slots: batch * splits per-sequence splits, or, for the balanced
 // partition (splits == 0), one per (workgroup, sequence) piece: at most

@@ -1053,10 +1053,10 @@ __global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode(const Decod
 // (workgroup, sequence) piece is written to partial slot w + b: the slots of
 // one sequence are consecutive, and the workgroup holding a sequence's first
 // page records (first slot, count) in a.meta[b].
-// floor(w T / G) in double precision, exact here: w <= G <= 256 and T < 2^40
-// pages (at most 65535 sequences of at most 2^24 pages) keep w T below 2^53,
-// and a quotient that is not an integer lies at least 1 / G away from one,
-// far beyond the division's rounding error (below 2^-13).
+// floor(w T / G) in double precision, exact here: w <= G <= 512 and T < 2^40
+// pages (at most 65535 sequences of at most 2^24 pages) keep w T below 2^49,
+// exact in a double, and a quotient that is not an integer lies at least 1 / G
+// away from one, far beyond the division's rounding error (below 2^-13).
 __device__ __forceinline__ int64_t share_start(int64_t w, int64_t T, int64_t G) {
   return (int64_t)floor((double)(w * T) / (double)G);
 }

@@ -77,11 +77,22 @@ typedef struct {
  * BF16 page: [token][d_c + d_r] bf16 = 73728 B (1152 B per token).
  * A token's slot is page_id * page_size + offset_in_page. */
 
-/* Bytes per token / per page of `fmt`; 0 if the format is unsupported. */
+/* Bytes per token / per page of `fmt`; 0 if the format is unsupported.
+ * Passage: the physical cache layout behind the compression figure ("QuantMLA:
+ * INT4 (and INT2) for both halves of the MLA cache", Key findings, systems;
+ * "Hugging Face Releases QuantMLA", Engineering Trade-offs and Performance).
+ * The pages give no byte breakdown: the layout above is this library's. */
 size_t mla_token_bytes(const mla_format_t* fmt);
 size_t mla_page_bytes(const mla_format_t* fmt);
 
 /* Quantize and pack n_new new tokens into the paged cache.
+ * Passage: the two cache paths, content latent INT4 or INT2 and RoPE key
+ * INT4, quantized separately ("QuantMLA: INT4 (and INT2) for both halves of
+ * the MLA cache", flowchart and Key findings, bits; "Hugging Face Releases
+ * QuantMLA", Engineering Trade-offs and Performance).  Group size, the
+ * asymmetric min/max rule and fp16 scale/zero are this library's reading
+ * (the pages name bit widths only); the arithmetic is stated with
+ * mla_format_t above.
  *   latent_bf16   [n_new, d_c]     content latent rows
  *   rope_bf16     [n_new, d_r]     RoPE key rows (RoPE already applied)
  *   slot_mapping  [n_new] int32    destination slot of each row; a negative
@@ -97,7 +108,9 @@ mla_status_t mla_quant_append(const mla_format_t* fmt,
                               const int32_t* slot_mapping, int32_t n_new,
                               void* cache, int64_t num_pages, void* stream);
 
-/* A per-sequence split count suited to this shape (from the batch size, the
+/* (No passage: the pages describe no kernel.  The split and workspace
+ * queries below describe this library's split-KV decode.)
+ * A per-sequence split count suited to this shape (from the batch size, the
  * longest sequence and the workgroups the compute units hold at once: two
  * per unit for the quantized formats at <= 32 heads), for callers that want
  * the fixed-split mode; always in [1, 64].  num_splits = 0 (the balanced
@@ -110,9 +123,12 @@ int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t nu
  * [batch, S, num_heads, d_c], then fp32 partial log-sum-exps
  * [batch, S, num_heads].  num_splits = 0: the same two arrays over
  * G + batch partial slots, then int32 [batch, 2] (first slot, slot count)
- * per sequence, where G (the balanced partition's workgroups) is 512 for the
- * quantized formats at <= 32 rows per sequence (two workgroups per compute
- * unit) and 256 otherwise.  Each array starts 256-byte aligned. */
+ * per sequence, where G (the balanced partition's workgroups) is the current
+ * device's compute units (at most 256 are used; an MI355X has 256) times the
+ * workgroups one unit holds: two for the quantized formats at <= 32 rows per
+ * sequence, else one (so G = 512 or 256 on an MI355X).  Each array starts
+ * 256-byte aligned.  Sizes are for the device current at the call: query them
+ * with the device that will run the decode current. */
 size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
                                   int32_t num_splits);
 
@@ -122,7 +138,15 @@ size_t mla_decode_workspace_bytes(const mla_format_t* fmt, int32_t batch, int32_
 int64_t mla_decode_partial_slots(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
                                  int32_t num_splits);
 
-/* Decode attention over the packed cache, for one query token per sequence:
+/* Decode attention over the packed cache, for one query token per sequence.
+ * Passage: the native low-bit MLA attention kernel that unpacks and
+ * dequantizes the cache inside attention ("QuantMLA: INT4 (and INT2) for both
+ * halves of the MLA cache", flowchart and Key findings, systems; "Hugging Face
+ * Releases QuantMLA", Engineering Trade-offs and Performance); the content
+ * latent is the shared source of keys and values (same wiki note, TL;DR and
+ * flowchart), so it is both key and value here, and the learned path
+ * transforms are folded into the weights offline (Key findings), so the
+ * kernel applies none:
  *   out[b, h, :] = sum_t softmax_t(scale * <q[b,h,:], khat[t,:]>) * khat[t, :d_c]
  *   lse[b, h]    = log sum_t exp(scale * <q[b,h,:], khat[t,:]>)   (natural log)
  * where khat[t] is token t's dequantized [latent | RoPE key] (576 values) and
@@ -140,9 +164,9 @@ int64_t mla_decode_partial_slots(const mla_format_t* fmt, int32_t batch, int32_t
  *   max_seq_len   host upper bound on seq_lens (sizes the fixed splits)
  *   num_splits    0 = balanced: the batch's pages, in sequence order, are cut
  *                 into min(G, pages) equal shares, one workgroup per share
- *                 (G = 256, one per compute unit, or 512 for the quantized
- *                 formats at <= 32 heads, two per unit), whatever the length
- *                 mix; 1..64 = every
+ *                 (G as for mla_decode_workspace_bytes: one or two per
+ *                 compute unit, 256 or 512 on an MI355X), whatever the
+ *                 length mix; 1..64 = every
  *                 sequence cut into that many contiguous page ranges.  Either
  *                 way the pieces are merged by log-sum-exp
  *   workspace     >= mla_decode_workspace_bytes(fmt, batch, num_heads,
@@ -161,7 +185,10 @@ mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16,
                                void* workspace, size_t workspace_bytes,
                                void* out_bf16, float* lse_out, void* stream);
 
-/* The serving step fused into one call: for every sequence b with
+/* The serving step fused into one call (the pages' cache-pressure serving
+ * setting, "QuantMLA's INT4/INT2 KV-cache quantization reports 5x long-context
+ * throughput over BF16", Where BF16 caches fall over: every decode step adds
+ * one token per sequence to the cache): for every sequence b with
  * seq_lens[b] >= 1, row b of latent_new_bf16 [batch, d_c] and rope_new_bf16
  * [batch, d_r] is quantized and packed into position seq_lens[b] - 1 (page
  * block_table[b, (seq_lens[b] - 1) / page_size], offset (seq_lens[b] - 1) %
@@ -194,7 +221,8 @@ mla_status_t mla_decode_append_partial(const mla_format_t* fmt, const void* late
                                        size_t workspace_bytes, void* stream);
 
 /* Multi-token decode (several query tokens per sequence, e.g. multi-token
- * prediction or speculative decoding): the last num_queries tokens of every
+ * prediction or speculative decoding; no passage: the pages describe one query
+ * token, and this extends mla_decode_lowbit causally): the last num_queries tokens of every
  * sequence are queries; query i (0 <= i < num_queries) sits at position
  * seq_lens[b] - num_queries + i and attends to tokens [0, seq_lens[b] -
  * num_queries + 1 + i), i.e. to itself and the tokens before it (their rows
@@ -227,6 +255,9 @@ mla_status_t mla_decode_multi_partial(const mla_format_t* fmt, const void* q_bf1
 
 /* The two stages of mla_decode_lowbit, for callers that schedule them
  * separately (for example to merge partial results computed elsewhere).
+ * No passage: split-KV with a log-sum-exp merge is how this library spreads
+ * long contexts over the compute units; the merged result is the softmax
+ * of mla_decode_lowbit over all tokens.
  * mla_decode_partial writes, for split s of sequence b, the normalized
  * partial output over that split's pages and its log-sum-exp (-inf for an
  * empty split) into `workspace` (layout of mla_decode_workspace_bytes).
@@ -234,7 +265,7 @@ mla_status_t mla_decode_multi_partial(const mla_format_t* fmt, const void* q_bf1
  * num_splits = S >= 1, split s of sequence b covers pages [s * P, (s + 1) * P)
  * with P = ceil(ceil(max_seq_len / page_size) / S), the last split running to
  * the end of the sequence.  With num_splits = 0, T = the batch's pages in all
- * and G = min(512 or 256 as for mla_decode_workspace_bytes, T), workgroup w < G takes pages
+ * and G = min(G of mla_decode_workspace_bytes, T), workgroup w < G takes pages
  * [floor(w * T / G), floor((w + 1) * T / G)) of the concatenation of all
  * sequences' pages (never empty), writes its piece of sequence b to slot
  * w + b, and records each sequence's (first slot, slot count) in the

@@ -1,6 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
-uses (balanced partition, num_splits = 0, partial + combine), checked on
-sampled sequences and heads that the CPU oracle can compute one by one."""
+uses (balanced partition, num_splits = 0, partial + combine).  The 32 x 8192
+C4R4 workload is checked on every element (whole cache bytes, every output
+and LSE); the larger ones on sampled sequences, all heads of each, that the
+CPU oracle computes one by one."""
 import math
 
 import numpy as np
@@ -15,7 +17,6 @@ pytestmark = pytest.mark.gpu
 
 ATOL, RTOL = 2e-3, 1e-2
 OFMT = {"C4R4": oracle.C4R4, "C2R4": oracle.C2R4, "BF16": oracle.BF16}
-HEADS = [0, 37, 64, 127]
 
 
 def _say(msg):
@@ -57,6 +58,13 @@ def _decode(w, fmt, lens, bt, cache):
     return q.cpu(), out.float().cpu().numpy(), lse.cpu().numpy(), S
 
 
+def _assert_outputs(o, ref, what):
+    err = np.abs(o - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), "%s: %d of %d outputs outside tolerance (max err %.3g)" % (
+        what, int(bad.sum()), bad.size, float(err.max()))
+
+
 def _check_sequence(w, fmt, b, lens, bt, cache, q, out, lse):
     L = int(lens[b])
     npg = (L + 63) // 64
@@ -69,20 +77,35 @@ def _check_sequence(w, fmt, b, lens, bt, cache, q, out, lse):
     slots = np.arange(L, dtype=np.int32)
     oracle.quant_append(OFMT[fmt], lat.cpu(), rope.cpu(), slots, ref_cache, npg)
     assert np.array_equal(got_pages, ref_cache), "sequence %d: %d cache bytes differ" % (b, int((got_pages != ref_cache).sum()))
-    # decode on sampled heads
-    heads = [h for h in HEADS if h < w.heads]
-    qh = q[b:b + 1, heads].contiguous()
-    ref, ref_lse = oracle.decode(OFMT[fmt], qh, got_pages, npg, np.arange(npg, dtype=np.int32)[None],
-                                 np.array([L], np.int32), w.softmax_scale)
-    o = out[b, heads]
-    err = np.abs(o - ref[0])
-    bad = err > ATOL + RTOL * np.abs(ref[0])
-    assert not bad.any(), "sequence %d: %d of %d outputs outside tolerance (max err %.3g)" % (
-        b, int(bad.sum()), bad.size, float(err.max()))
-    assert np.allclose(lse[b, heads], ref_lse[0], rtol=1e-5, atol=1e-4)
+    # decode, every head of the sequence
+    ref, ref_lse = oracle.decode(OFMT[fmt], q[b:b + 1].contiguous(), got_pages, npg,
+                                 np.arange(npg, dtype=np.int32)[None], np.array([L], np.int32), w.softmax_scale)
+    _assert_outputs(out[b], ref[0], "sequence %d" % b)
+    assert np.allclose(lse[b], ref_lse[0], rtol=1e-5, atol=1e-4)
 
 
-@pytest.mark.parametrize("name", ["dsv3_c4r4_8k", "c2r4_32k_outliers", "c4r4_128k", "mixed_c2r4_serving"])
+def test_fullsize_every_element_dsv3_8k():
+    """32 x 8192 tokens, 128 heads, C4R4: the whole cache bit-exact against the
+    oracle's quantizer and every output and LSE against the oracle's decode."""
+    w = W.WORKLOADS["dsv3_c4r4_8k"]
+    _say("full-size %s, every element: B=%d H=%d" % (w.name, w.batch, w.heads))
+    lens, bt, npages, cache = _build(w, w.fmt)
+    q, out, lse, S = _decode(w, w.fmt, lens, bt, cache)
+    host = cache.cpu().numpy()
+    ref_cache = np.zeros_like(host)
+    for b, L in enumerate(lens):
+        lat, rope = W.sequence_rows(w, b, 0, int(L), "cuda")   # the draws the cache was built from
+        oracle.quant_append(OFMT[w.fmt], lat.cpu(), rope.cpu(), W.slots_for(bt, b, 0, int(L)), ref_cache, npages)
+    assert np.array_equal(host, ref_cache), "%d cache bytes differ" % int((host != ref_cache).sum())
+    _say("  cache bit-exact; oracle decode of all %d sequences" % w.batch)
+    ref, ref_lse = oracle.decode(OFMT[w.fmt], q, host, npages, bt, lens, w.softmax_scale)
+    _assert_outputs(out, ref, w.name)
+    assert np.allclose(lse, ref_lse, rtol=1e-5, atol=1e-4)
+    del cache
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["c2r4_32k_outliers", "c4r4_128k", "mixed_c2r4_serving"])
 def test_fullsize_sampled(name):
     w = W.WORKLOADS[name]
     _say("full-size %s: B=%d H=%d fmt=%s" % (name, w.batch, w.heads, w.fmt))
