@@ -15,7 +15,8 @@ import os
 __all__ = [
     "FORMATS", "MlaError", "format_struct", "load_library",
     "mla_token_bytes", "mla_page_bytes", "mla_quant_append", "mla_decode_num_splits",
-    "mla_decode_workspace_bytes", "mla_decode_partial_slots", "mla_decode_lowbit", "mla_decode_partial", "mla_decode_combine",
+    "mla_decode_workspace_bytes", "mla_decode_partial_slots", "mla_decode_lowbit", "mla_decode_lowbit_noalloc",
+    "mla_decode_partial", "mla_decode_combine",
     "mla_decode_append_lowbit", "mla_decode_append_partial", "mla_decode_multi_lowbit",
     "mla_decode_multi_partial", "mla_absorb_q", "mla_project_out",
     "mla_last_error", "alloc_cache",
@@ -71,6 +72,7 @@ def load_library():
         "mla_decode_workspace_bytes": (SZ, [FP, I32, I32, I32]),
         "mla_decode_partial_slots": (I64, [FP, I32, I32, I32]),
         "mla_decode_lowbit": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P, P, P]),
+        "mla_decode_lowbit_noalloc": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, P, P]),
         "mla_decode_partial": (ctypes.c_int, [FP, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ, P]),
         "mla_decode_combine": (ctypes.c_int, [FP, I32, I32, I32, P, SZ, P, P, P]),
         "mla_decode_append_lowbit": (ctypes.c_int, [FP, P, P, P, P, I64, P, P, I32, I32, I32, I32, F, I32, P, SZ,
@@ -206,6 +208,25 @@ def mla_decode_lowbit(fmt, q, cache, block_table, seq_lens, softmax_scale, max_s
         _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
         int(max_seq_len), float(softmax_scale), int(num_splits),
         _opt(workspace, "workspace", torch.uint8), workspace.numel() if workspace is not None else 0,
+        _dev(out, "out", torch.bfloat16), _opt(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse
+
+
+def mla_decode_lowbit_noalloc(fmt, q, cache, block_table, seq_lens, softmax_scale, max_seq_len=None, num_splits=0,
+                              out=None, lse=None, num_pages=None, stream=None):
+    """mla_decode_lowbit whose partial results live in the library's per-device
+    scratch (no workspace argument; the C call allocates nothing).  Pass `out`
+    (and `lse`) to allocate nothing on this side either.  Returns (out, lse)."""
+    import torch
+    B, H, MP, NP = _decode_shapes(q, cache, block_table, seq_lens, fmt, num_pages)
+    if max_seq_len is None:
+        max_seq_len = MP * 64
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    _check(load_library().mla_decode_lowbit_noalloc(
+        ctypes.byref(format_struct(fmt)), _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.uint8), NP,
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), B, H, MP,
+        int(max_seq_len), float(softmax_scale), int(num_splits),
         _dev(out, "out", torch.bfloat16), _opt(lse, "lse", torch.float32), _stream(stream)))
     return out, lse
 

@@ -10,6 +10,14 @@
 
 #include "kernels.h"
 
+// Device scratch of mla_decode_lowbit_noalloc: the decode's partial results
+// (the workspace of mla_decode_lowbit) for callers that cannot allocate.
+// Every device the library runs on holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory): it uses the per-device address that
+// hipGetSymbolAddress returns (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -223,6 +231,27 @@ mla_status_t decode_partial(const mla_format_t* fmt, const void* q_bf16, int32_t
   return MLA_OK;
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with that device current) and kept per device.
+mla_status_t noalloc_scratch(void** ptr) {
+  static std::atomic<void*> known[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "device %d: the no-allocation entry point serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  void* p = known[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    known[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return MLA_OK;
+}
+
 mla_status_t decode_combine(const mla_format_t* fmt, int32_t batch, int32_t num_heads, int32_t num_splits,
                             const void* workspace, size_t ws_bytes, void* out_bf16, float* lse_out, void* stream) {
   if (format_id(fmt) < 0) return fail(MLA_ERR_UNSUPPORTED, "unsupported cache format");
@@ -348,6 +377,31 @@ mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16, cons
                                void* out_bf16, float* lse_out, void* stream) {
   return decode_full(fmt, q_bf16, 1, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
                      max_seq_len, softmax_scale, num_splits, workspace, ws_bytes, out_bf16, lse_out, Append{}, stream);
+}
+
+mla_status_t mla_decode_lowbit_noalloc(const mla_format_t* fmt, const void* q_bf16, const void* cache,
+                                       int64_t num_pages, const int32_t* block_table, const int32_t* seq_lens,
+                                       int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
+                                       int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* out_bf16,
+                                       float* lse_out, void* stream) {
+  DecodeShape sh;
+  mla_status_t st = check_decode(fmt, q_bf16, cache, num_pages, block_table, seq_lens, batch, num_heads,
+                                 max_pages_per_seq, max_seq_len, softmax_scale, num_splits, &sh);
+  if (st != MLA_OK || batch == 0) return st;
+  void* ws = nullptr;
+  if (num_splits != 1) {  // one split writes the output directly: no scratch
+    const size_t need = workspace_bytes(sh.fmt, batch, num_heads, num_splits);
+    if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+      return fail(MLA_ERR_WORKSPACE,
+                  "this shape needs %zu bytes of decode scratch; the no-allocation entry point holds %zu per device "
+                  "(use fewer sequences per call, fixed splits, or mla_decode_lowbit with a workspace)",
+                  need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+    st = noalloc_scratch(&ws);
+    if (st != MLA_OK) return st;
+  }
+  return decode_full(fmt, q_bf16, 1, cache, num_pages, block_table, seq_lens, batch, num_heads, max_pages_per_seq,
+                     max_seq_len, softmax_scale, num_splits, ws, ws ? (size_t)MLA_NOALLOC_SCRATCH_BYTES : 0,
+                     out_bf16, lse_out, Append{}, stream);
 }
 
 mla_status_t mla_decode_append_partial(const mla_format_t* fmt, const void* latent_new_bf16,

@@ -185,6 +185,37 @@ mla_status_t mla_decode_lowbit(const mla_format_t* fmt, const void* q_bf16,
                                void* workspace, size_t workspace_bytes,
                                void* out_bf16, float* lse_out, void* stream);
 
+/* Bytes of device scratch mla_decode_lowbit_noalloc holds on every device the
+ * library runs on (128 MiB). */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* mla_decode_lowbit without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of mla_decode_lowbit (same kernels, bitwise the same out and lse); the
+ * partial results live in a device array of MLA_NOALLOC_SCRATCH_BYTES that
+ * the library holds per device until the process ends.  This call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *  - A shape whose workspace (mla_decode_workspace_bytes(fmt, batch,
+ *    num_heads, num_splits)) exceeds MLA_NOALLOC_SCRATCH_BYTES is refused
+ *    with MLA_ERR_WORKSPACE before anything is launched.  With the balanced
+ *    partition at 128 heads that is about 250 sequences per call.
+ *    num_splits = 1 uses no scratch.
+ *  - Every call on a device shares that device's array, which keeps the last
+ *    call's contents (nothing in it needs to start at zero: the decode
+ *    writes every entry the combine reads).  Calls that overlap on one
+ *    device (on different streams, or from different threads) race on it:
+ *    serialize them.
+ *  - The first call on a device looks the array's address up
+ *    (hipGetSymbolAddress) with that device current; make that first call
+ *    outside graph capture. */
+mla_status_t mla_decode_lowbit_noalloc(const mla_format_t* fmt, const void* q_bf16,
+                                       const void* cache, int64_t num_pages,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       int32_t batch, int32_t num_heads, int32_t max_pages_per_seq,
+                                       int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                       void* out_bf16, float* lse_out, void* stream);
+
 /* The serving step fused into one call (the pages' cache-pressure serving
  * setting, "QuantMLA's INT4/INT2 KV-cache quantization reports 5x long-context
  * throughput over BF16", Where BF16 caches fall over: every decode step adds

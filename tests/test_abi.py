@@ -194,3 +194,23 @@ def test_multi_token_argument_errors():
     assert call(ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
     # the combine takes rows = num_queries * num_heads (up to 2048)
     assert L.mla_decode_combine(_fmt(), 2, 2049, 0, A2, 1 << 40, A, None, None) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_argument_errors():
+    """The no-allocation decode validates like mla_decode_lowbit and refuses a
+    shape whose partial results exceed its per-device scratch (128 MiB) before
+    looking up any device memory."""
+    L = mla.load_library()
+
+    def call(batch=2, heads=128, splits=0, out=A, q=A):
+        return L.mla_decode_lowbit_noalloc(_fmt(), q, A, 10, A, A, batch, heads, 4, 256, 0.07, splits, out, None,
+                                           None)
+    assert call(heads=129) == mla.MLA_ERR_UNSUPPORTED
+    assert call(splits=65) == mla.MLA_ERR_INVALID_ARG
+    assert call(q=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(batch=0, q=None, out=None) == mla.MLA_OK
+    assert mla.mla_decode_workspace_bytes("C4R4", 600, 128, 0) > 128 << 20
+    assert call(batch=600) == mla.MLA_ERR_WORKSPACE
+    assert "scratch" in mla.mla_last_error()
+    assert call(batch=600, splits=1, out=None) == mla.MLA_ERR_INVALID_ARG   # one split needs no scratch: out checked
+
