@@ -81,7 +81,8 @@ int compute_units() {
 }
 
 // Workgroups that run at once: one per compute unit, two where the decode
-// kernel splits channels (<= 32 rows per sequence, quantized formats).
+// kernel splits channels over four wavefronts (17..32 rows per sequence,
+// quantized formats).
 int resident_groups(int fmt, int rows) { return compute_units() * mla::workgroups_per_cu(fmt, rows); }
 
 // Partial-row slots: batch * splits per-sequence splits, or, for the balanced

@@ -8,10 +8,12 @@
 //
 // One workgroup = one piece of work (a page range of one sequence: a fixed
 // split, or a share of the balanced partition), 256 threads = 4 wavefronts,
-// one per SIMD.  Wave w owns heads [32w, 32w + 32); at <= 64 rows per
+// one per SIMD.  Wave w owns heads [32w, 32w + 32); at 17..64 rows per
 // sequence the wavefronts of a head group split its channels instead (four
-// per group at <= 32 rows, two workgroups per compute unit; two per group at
-// 33..64 rows), sharing one softmax through LDS, see split_pass_cs.  The work
+// per group at 17..32 rows, two workgroups per compute unit; two per group at
+// 33..64 rows), sharing one softmax through LDS, see split_pass_cs; at <= 16
+// rows (quantized formats) eight independent wavefronts each carry their own
+// 16-token sub-tiles, see process_range_iw.  The work
 // is tiled by half pages (32 tokens):
 //   1. fill: every thread loads its share of the next tile's packed bytes
 //      (16-byte loads; the 32 lanes of a half-wave read 512 contiguous bytes of
@@ -888,6 +890,510 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t 
   }
 }
 
+// ---------------------------------------------------------------- independent wavefronts (<= 16 rows)
+// At <= 16 rows per sequence one 16 x 16 MFMA block holds every row, so a
+// wavefront can carry 16 tokens through the whole attention step on its own.
+// Eight wavefronts per workgroup (two per SIMD, one workgroup per compute
+// unit) take every eighth 16-token sub-tile of the piece, each:
+//   1. loads the packed bytes of its next sub-tile while this one computes;
+//      lane (t, g) = (lane % 16, lane / 16) owns token t of the sub-tile and
+//      a quarter of its channels: the 8 values of k-step ks that Q.K^T needs
+//      in its lane (channels chan(ks, g) .. + 8) are one code dword;
+//   2. dequantizes k-step by k-step in registers, straight into the A operand
+//      of MFMA 16x16x32 bf16 (16 tokens x 32 channels), B = q^T read from LDS
+//      (the rows of the piece are staged once per piece); the content values
+//      also go to the wavefront's own LDS buffer for step 4.  Output: S^T, lane
+//      (h, g) holding row h for tokens 4 g .. 4 g + 3;
+//   3. takes the four softmax weights of its lane against a fixed reference
+//      per wavefront and pass (as in split_pass), splits them into high and
+//      low bf16 halves, and trades halves with lane l ^ 32 (one
+//      v_permlane32_swap per pair) so that lanes 0..31 hold the high halves of
+//      16 tokens and lanes 32..63 the low halves;
+//   4. P.V on MFMA 16x16x32 bf16 with k = 16 tokens x {high, low}: A = V^T
+//      (16 channels x the same 16 tokens twice) from transposing LDS reads of
+//      its buffer, O^T (512 channels x 16 rows) in 32 x 4 accumulators.
+// No barrier is taken per sub-tile: while one wavefront of a SIMD
+// dequantizes, the other's MFMAs run.  At the end of a piece the eight
+// partial results (each against its own reference) are merged through LDS
+// with log-sum-exp weights.
+constexpr int kIwWaves = 8;
+constexpr int kIwThreads = 64 * kIwWaves;
+constexpr int kSubTok = 16;                       // tokens per sub-tile
+constexpr int kVRow = kDc + 16;                   // bf16 per row of a V buffer (1056 bytes; see vrow)
+constexpr int kVBuf = kSubTok * kVRow;            // bf16 per wavefront buffer
+constexpr int kIwQRow = kD + 8;                   // bf16 per staged q row (1168 bytes)
+constexpr int kIwRedRow = kDc + 4;                // fp32 per row in the end-of-piece merge
+constexpr size_t kIwRedOff = ((size_t)kIwWaves * kVBuf + 16 * kIwQRow) * sizeof(__bf16);  // 151808 bytes
+static_assert(4 * 16 * kIwRedRow * sizeof(float) <= (size_t)kIwWaves * kVBuf * sizeof(__bf16),
+              "four wavefronts' outputs fit in the V buffers");
+
+// value of lane l ^ 16 / l ^ 32 (through ds_bpermute; used once per pass)
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), m));
+}
+
+// 8 INT4 codes of a dword (element e in bits 4 e) -> bf16(fma(code, S, Z)), S
+// scaled by kCodeScale as in code_pair
+__device__ __forceinline__ bf16x8 dq_int4x8(unsigned w, float S, float Z) {
+  const unsigned lo = mask_bytes(w, 0x0F0F0F0Fu);       // elements 0, 2, 4, 6
+  const unsigned hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);  // elements 1, 3, 5, 7
+  const f32x2 l0 = code_pair(lo, 0), l1 = code_pair(lo, 1), h0 = code_pair(hi, 0), h1 = code_pair(hi, 1);
+  const u32x4 o = {pack_bf16x2(__builtin_fmaf(l0[0], S, Z), __builtin_fmaf(h0[0], S, Z)),
+                   pack_bf16x2(__builtin_fmaf(l0[1], S, Z), __builtin_fmaf(h0[1], S, Z)),
+                   pack_bf16x2(__builtin_fmaf(l1[0], S, Z), __builtin_fmaf(h1[0], S, Z)),
+                   pack_bf16x2(__builtin_fmaf(l1[1], S, Z), __builtin_fmaf(h1[1], S, Z))};
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// elements 8 hf .. 8 hf + 7 of 16 INT2 codes (element e in bits 2 e), given
+// b[j] = (w >> 2 j) & 0x03030303 (byte k of b[j] is element 4 k + j)
+__device__ __forceinline__ bf16x8 dq_int2x8(const unsigned (&b)[4], int hf, float S, float Z) {
+  const f32x2 f0 = code_pair(b[0], hf), f1 = code_pair(b[1], hf), f2 = code_pair(b[2], hf), f3 = code_pair(b[3], hf);
+  const u32x4 o = {pack_bf16x2(__builtin_fmaf(f0[0], S, Z), __builtin_fmaf(f1[0], S, Z)),
+                   pack_bf16x2(__builtin_fmaf(f2[0], S, Z), __builtin_fmaf(f3[0], S, Z)),
+                   pack_bf16x2(__builtin_fmaf(f0[1], S, Z), __builtin_fmaf(f1[1], S, Z)),
+                   pack_bf16x2(__builtin_fmaf(f2[1], S, Z), __builtin_fmaf(f3[1], S, Z))};
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// Packed bytes of one lane's share of a sub-tile (token t of the page, lane
+// group g) and the dequantization of its k-steps.  Both formats give lane
+// group g the same channels: content k-step ks = 4 m + d (block m = 128
+// channels) holds channels 128 m + 32 g + 8 d .. + 8 of the lane's token, and
+// RoPE k-steps 16, 17 hold channels 512 + 32 (ks - 16) + 8 g .. + 8 (chan()).
+// The q operand and the V buffer use the same offsets.  The registers hold
+// one sub-tile: part i (content block m = i, or the RoPE part i = 4) is
+// reloaded with the next sub-tile's bytes right after its last k-step, so
+// the loads of the next sub-tile are in flight while this one computes.
+// Addresses: a wavefront-uniform page base plus per-lane offsets fixed for
+// the pass.
+__device__ __forceinline__ constexpr int iw_chan(int ks, int g) {
+  return ks < 16 ? 128 * (ks >> 2) + 32 * g + 8 * (ks & 3) : kDc + 32 * (ks - 16) + 8 * g;
+}
+
+struct SubLanes {
+  int c, sz, rc, rsz;  // per-lane byte offsets: content codes, content S/Z, RoPE codes, RoPE S/Z
+};
+
+template <int F> struct SubFill;
+
+template <> struct SubFill<kC4R4> {
+  using Lay = PageLayout<kC4R4>;
+  // block m of lane group g: chunk 4 m + g (16 bytes: 32 channels), group 2 m + g / 2
+  static __device__ __forceinline__ SubLanes lanes(int t, int g) {
+    return SubLanes{16 * t + 1024 * g, 4 * t + 256 * (g >> 1), 16 * t + 4 * g, 4 * t};
+  }
+  u32x4 c[4];
+  unsigned sz[4];
+  unsigned r[2];    // dword g of RoPE chunks 0, 1
+  unsigned rsz;
+  const uint8_t* pb;  // page base of the sub-tile whose bytes issue() loads
+  int hp;             // its quarter of the page
+  __device__ __forceinline__ void issue(int i, const SubLanes& o) {
+    if (i < 4) {
+      c[i] = *(const u32x4*)(pb + Lay::kCodesA + 256 * hp + 4096 * i + o.c);
+      sz[i] = *(const unsigned*)(pb + Lay::kSzB + 64 * hp + 512 * i + o.sz);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) r[j] = *(const unsigned*)(pb + Lay::kCodesC + 256 * hp + 1024 * j + o.rc);
+      rsz = *(const unsigned*)(pb + Lay::kSzD + 64 * hp + o.rsz);
+    }
+  }
+  __device__ __forceinline__ unsigned sz_of(int ks, bool live) const {
+    return live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u;
+  }
+  __device__ __forceinline__ bf16x8 step(int ks, float S, float Z) {
+    return dq_int4x8(ks < 16 ? c[ks >> 2][ks & 3] : r[ks - 16], S, Z);
+  }
+};
+
+template <> struct SubFill<kC2R4> {
+  using Lay = PageLayout<kC2R4>;
+  // block m of lane group g: bytes 8 (g & 1) .. + 8 of chunk 2 m + g / 2 (32
+  // channels), group 4 m + g
+  static __device__ __forceinline__ SubLanes lanes(int t, int g) {
+    return SubLanes{16 * t + 1024 * (g >> 1) + 8 * (g & 1), 4 * t + 256 * g, 16 * t + 4 * g, 4 * t};
+  }
+  u32x2 c[4];
+  unsigned sz[4];
+  unsigned r[2];
+  unsigned rsz;
+  unsigned b[4];    // masked code bytes of the dword being converted
+  const uint8_t* pb;
+  int hp;
+  __device__ __forceinline__ void issue(int i, const SubLanes& o) {
+    if (i < 4) {
+      c[i] = *(const u32x2*)(pb + Lay::kCodesA + 256 * hp + 2048 * i + o.c);
+      sz[i] = *(const unsigned*)(pb + Lay::kSzB + 64 * hp + 1024 * i + o.sz);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) r[j] = *(const unsigned*)(pb + Lay::kCodesC + 256 * hp + 1024 * j + o.rc);
+      rsz = *(const unsigned*)(pb + Lay::kSzD + 64 * hp + o.rsz);
+    }
+  }
+  __device__ __forceinline__ unsigned sz_of(int ks, bool live) const {
+    return live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u;
+  }
+  // k-step 4 m + d: half d & 1 of dword d / 2 of block m
+  __device__ __forceinline__ bf16x8 step(int ks, float S, float Z) {
+    if (ks >= 16) return dq_int4x8(r[ks - 16], S, Z);
+    if ((ks & 1) == 0) {
+      const unsigned w = c[ks >> 2][(ks & 3) >> 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = mask_bytes(w >> (2 * j), 0x03030303u);
+    }
+    return dq_int2x8(b, ks & 1, S, Z);
+  }
+};
+
+// Block-table window over sub-tiles (4 per page), as PageWindow.
+struct SubPageWindow {
+  const int32_t* bt;
+  int p_end, wbase, ids;
+  __device__ __forceinline__ SubPageWindow(const int32_t* bt_, int u0, int u1) : bt(bt_) {
+    p_end = (u1 + 3) >> 2;
+    wbase = u0 >> 2;
+    const int lane = threadIdx.x & 63;
+    ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
+  }
+  __device__ __forceinline__ int page_of(int u) {
+    const int pg = u >> 2;
+    if (pg - wbase >= 64) {  // uniform per wavefront; every 64 pages
+      wbase = pg;
+      const int lane = threadIdx.x & 63;
+      ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
+      return __builtin_amdgcn_readlane(ids, 0);
+    }
+    return __builtin_amdgcn_readlane(ids, pg - wbase);
+  }
+};
+
+struct IwAcc {
+  f32x4 o[32];   // o[ct][r]: O^T[16 ct + 4 g + r][lane's row], against 2^m_ref
+  float l_sum;   // this lane's tokens' share of sum_t p_t
+  float m_ref;   // reference (log2 units) of this wavefront's weights
+  float m_seen;  // max logit (log2 units) of this lane's tokens
+};
+
+// Row t of a wavefront's V buffer starts at element vrow(t): rows 528 bf16
+// (1056 bytes) apart, rows 8..15 shifted by 16 bytes.
+__device__ __forceinline__ constexpr int vrow(int t) { return t * kVRow + 8 * (t >> 3); }
+
+// Q.K^T k-step order: the RoPE k-steps first (they write no V), then the
+// content blocks in channel order.
+__device__ __forceinline__ constexpr int iw_ks(int p) { return p < 2 ? 16 + p : p - 2; }
+// P.V channel tiles issued with Q.K^T step p of the next sub-tile: 4 each
+// with the RoPE steps (block 0), then 2 per content step of blocks 0..2 (the
+// tiles of block m + 1), none during block 3.  Every tile of block m is read
+// before step 2 + 4 m writes block m of the next sub-tile.
+__device__ __forceinline__ constexpr int pv_begin(int p) { return p < 2 ? 4 * p : p < 14 ? 8 + 2 * (p - 2) : 32; }
+__device__ __forceinline__ constexpr int pv_end(int p) { return p < 2 ? 4 * p + 4 : p < 14 ? 10 + 2 * (p - 2) : 32; }
+
+// One pass of wavefront `wave` over its sub-tiles u0 + wave + 8 i < u1 of the
+// piece, software-pipelined: the P.V of sub-tile i runs between the Q.K^T
+// k-steps (dequantization, MFMA) of sub-tile i + 1.  Returns true if a
+// weight may have overflowed (a logit more than kMaxLift above the
+// reference): the caller redoes the piece with a fixed reference.
+template <int F>
+__device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int u0, int u1,
+                                        int limit, bool fixed, float m_fixed, IwAcc& acc) {
+  using SF = SubFill<F>;
+  const int limit_min = L - (a.s_q - 1);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = lane & 15, g = lane >> 4;  // QK operand lane: token t, channel quarter g; S^T lane: row t, tokens 4 g..
+  __bf16* __restrict__ vbuf = smem + wave * kVBuf;
+  const __bf16* __restrict__ qlds = smem + kIwWaves * kVBuf + t * kIwQRow;
+#pragma unroll
+  for (int ct = 0; ct < 32; ++ct) acc.o[ct] = (f32x4){};
+  acc.l_sum = 0.0f;
+  acc.m_ref = fixed ? finite_ref(m_fixed) : -INFINITY;
+  acc.m_seen = -INFINITY;
+  bool lifted = false;
+  bool first = !fixed;
+  const int ufirst = u0 + wave;
+  if (ufirst >= u1) return false;
+  SubPageWindow win(bt, ufirst, u1);
+  // transposing-read addresses of the P.V operand: block kg = lane / 16 reads
+  // tokens 4 (kg & 1) + j (then + 8), lane 4 j + r of the block channels
+  // 4 r .. + 4 of the channel tile; lane i of the block receives channel i of
+  // those 4 tokens
+  const int tr_tok = 4 * (g & 1) + ((lane & 15) >> 2);
+  const __bf16* __restrict__ vtr = vbuf + vrow(tr_tok) + 4 * (lane & 3);
+  auto tr_read = [&](int ct) {
+    const __bf16* v0 = vtr + 16 * ct;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v0);
+    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + vrow(8)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  __bf16* __restrict__ vw = vbuf + vrow(t);
+  const SubLanes lo = SF::lanes(t, g);
+
+  SF f;
+  int pg_next = win.page_of(ufirst);
+  auto aim = [&](int page, int u) {  // the sub-tile whose bytes issue() loads next
+    const bool ok = page >= 0 && page < a.num_pages;
+    f.pb = a.cache + (ok ? page : 0) * (int64_t)PageLayout<F>::kBytes;  // an invalid page reads page 0, zeroed
+    f.hp = u & 3;
+  };
+  aim(pg_next, ufirst);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) f.issue(i, lo);
+
+  // ---- Q.K^T state of the sub-tile being dequantized
+  f32x4 s0, s1;
+  bf16x8 qv[4];
+  float S = 0.0f, Z = 0.0f;
+  bool live = false;
+  auto qk_begin = [&](int u) {
+    const int pg = pg_next;
+    live = pg >= 0 && pg < a.num_pages && kSubTok * u + t < L;
+    const int un = u + kIwWaves < u1 ? u + kIwWaves : u;  // the last one reloads itself: harmless
+    pg_next = win.page_of(un);
+    aim(pg_next, un);
+    s0 = (f32x4){};
+    s1 = (f32x4){};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) qv[d] = *(const bf16x8*)(qlds + iw_chan(iw_ks(d), g));
+  };
+  auto qk_step = [&](int p) {
+    const int ks = iw_ks(p);
+    if (ks % 4 == 0 || ks == 16) sz_unpack(f.sz_of(ks, live), S, Z);
+    const bf16x8 kv = f.step(ks, S, Z);
+    const bf16x8 qk = qv[p & 3];
+    if (p + 4 < 18) qv[p & 3] = *(const bf16x8*)(qlds + iw_chan(iw_ks(p + 4), g));
+    if (ks < 16) *(bf16x8*)(vw + iw_chan(ks, g)) = kv;
+    if (p & 1)
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qk, s1, 0, 0, 0);
+    else
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qk, s0, 0, 0, 0);
+    if (p == 1) f.issue(4, lo);                           // RoPE part consumed
+    if (p >= 2 && (ks & 3) == 3) f.issue(ks >> 2, lo);     // content block consumed
+  };
+  // ---- softmax of a finished Q.K^T: weights against the reference, high /
+  //      low bf16 halves exchanged with lane l ^ 32 into the P.V operand
+  bf16x8 bp;
+  auto softmax = [&](int u) {
+    f32x4 s = s0 + s1;
+    if (kSubTok * (u + 1) > limit_min) {  // the tokens past the row's limit (and the sequence end)
+      const int lt = limit - kSubTok * u - 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r >= lt) s[r] = -INFINITY;
+    }
+    const float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (first) {  // this wavefront's reference: its first sub-tile's max (over the 16 tokens), lifted
+      float m = fmaxf(smax, lane_xor(smax, 16));
+      m = fmaxf(m, lane_xor(m, 32));
+      acc.m_ref = finite_ref(m * a.scale_log2 + kRefLift);
+      first = false;
+    }
+    {
+      const float mt = smax * a.scale_log2;
+      acc.m_seen = fmaxf(acc.m_seen, mt);
+      lifted |= mt - acc.m_ref > kMaxLift;
+    }
+    const float neg_ref = -acc.m_ref;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, neg_ref));
+    acc.l_sum += (p[0] + p[1]) + (p[2] + p[3]);
+    const unsigned h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+    const unsigned l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const unsigned l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    // lanes < 32 receive the high halves of lane l + 32, lanes >= 32 the low halves of lane l - 32
+    const auto x01 = __builtin_amdgcn_permlane32_swap(h01, l01, false, false);
+    const auto x23 = __builtin_amdgcn_permlane32_swap(h23, l23, false, false);
+    // k slots 0..3: tokens 4 (g & 1) + [0, 4), slots 4..7: those + 8; high
+    // halves in lanes 0..31, low halves in lanes 32..63
+    const u32x4 bw = lane < 32 ? (u32x4){h01, h23, x01[1], x23[1]} : (u32x4){x01[0], x23[0], l01, l23};
+    bp = __builtin_bit_cast(bf16x8, bw);
+  };
+  // ---- P.V of the previous sub-tile: O^T += V^T . [P_hi; P_lo], channel
+  //      tile ct, operands read 4 tiles ahead
+  bf16x8 va[5];
+  auto pv_start = [&]() {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) va[d] = tr_read(d);
+  };
+  auto pv_tile = [&](int ct) {
+    if (ct + 4 < 32) va[(ct + 4) % 5] = tr_read(ct + 4);
+    acc.o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct % 5], bp, acc.o[ct], 0, 0, 0);
+  };
+
+  // prologue: Q.K^T and weights of the first sub-tile
+  qk_begin(ufirst);
+#pragma unroll
+  for (int p = 0; p < 18; ++p) qk_step(p);
+  softmax(ufirst);
+  int u = ufirst;
+  for (; u + kIwWaves < u1; u += kIwWaves) {
+    // P.V of sub-tile u interleaved with Q.K^T of sub-tile u + 8
+    qk_begin(u + kIwWaves);
+    pv_start();
+#pragma unroll
+    for (int p = 0; p < 18; ++p) {
+      qk_step(p);
+#pragma unroll
+      for (int ct = pv_begin(p); ct < pv_end(p); ++ct) pv_tile(ct);
+    }
+    softmax(u + kIwWaves);
+  }
+  // epilogue: P.V of the last sub-tile
+  pv_start();
+#pragma unroll
+  for (int ct = 0; ct < 32; ++ct) pv_tile(ct);
+  return lifted;
+}
+
+// Merged result of a piece for the wavefronts' rows, written to `slot`
+// (partials) or to the output (direct mode).  Per-wavefront reference,
+// denominator and seen maximum come through `red`; the O blocks through the
+// V buffers in two rounds of four wavefronts, each wavefront summing 64 of
+// the 512 channels.
+struct IwRed {
+  float m[kIwWaves][16], l[kIwWaves][16], s[kIwWaves][16];
+};
+// V buffers, staged q, then the merge record
+constexpr size_t kIwLds = kIwRedOff + sizeof(IwRed);
+
+// Per-row totals of the piece: every lane of row t (lanes t, t + 16, t + 32,
+// t + 48 of every wavefront) gets M = max reference, L = sum l 2^(m - M) and
+// the seen maximum; also this wavefront's scale 2^(m_ref - M).
+__device__ __forceinline__ void iw_totals(IwRed& red, const IwAcc& acc, float& M, float& Ltot, float& seen,
+                                          float& f_own) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t = lane & 15;
+  float l = acc.l_sum + lane_xor(acc.l_sum, 16);
+  l += lane_xor(l, 32);
+  float sm = fmaxf(acc.m_seen, lane_xor(acc.m_seen, 16));
+  sm = fmaxf(sm, lane_xor(sm, 32));
+  if (lane < 16) {
+    red.m[wave][t] = l > 0.0f ? acc.m_ref : -INFINITY;
+    red.l[wave][t] = l;
+    red.s[wave][t] = sm;
+  }
+  __syncthreads();
+  M = -INFINITY;
+  seen = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kIwWaves; ++w) {
+    M = fmaxf(M, red.m[w][t]);
+    seen = fmaxf(seen, red.s[w][t]);
+  }
+  Ltot = 0.0f;
+  f_own = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kIwWaves; ++w)
+      if (red.l[w][t] > 0.0f) Ltot += red.l[w][t] * __builtin_amdgcn_exp2f(red.m[w][t] - M);
+    if (l > 0.0f) f_own = __builtin_amdgcn_exp2f(acc.m_ref - M);
+  }
+}
+
+template <bool kDirect>
+__device__ __forceinline__ void iw_write(const DecodeArgs& a, __bf16* smem, int b, int64_t slot, int chunk, int L,
+                                         IwAcc& acc, float M, float f_own) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t = lane & 15, g = lane >> 4;
+  float* red = (float*)smem;  // 4 x [16 rows][kIwRedRow] fp32 over the V buffers
+  // this lane's summing share: row t, channels 64 wave + 16 g .. + 16
+  f32x4 sum[4] = {};
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    __syncthreads();  // the V buffers are free (round 0) / read (round 1)
+    if ((wave >> 2) == round) {
+      float* dst = red + (wave & 3) * 16 * kIwRedRow + t * kIwRedRow + 4 * g;
+#pragma unroll
+      for (int ct = 0; ct < 32; ++ct) *(f32x4*)(dst + 16 * ct) = acc.o[ct] * f_own;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int src = 0; src < 4; ++src) {
+      const float* s = red + src * 16 * kIwRedRow + t * kIwRedRow + 64 * wave + 16 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += *(const f32x4*)(s + 4 * i);
+    }
+  }
+  // row t of the workgroup: the totals are per row (any lane of row t holds them)
+  const RowOf row = row_of(a, chunk, L, t);
+  if (t >= a.s_q * a.chunk_heads || !row.valid) return;
+  const float Ltot = acc.l_sum;  // (the caller stores the row total here)
+  const float inv = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
+  const float lse = Ltot > 0.0f ? (M + __log2f(Ltot)) * 0.69314718055994531f : -INFINITY;
+  const int R = a.heads;
+  const int ch = 64 * wave + 16 * g;
+  if (kDirect) {
+    __bf16* orow = a.out + ((int64_t)b * R + row.g) * kDc + ch;
+    u32x4 w0, w1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      w0[2 * i] = pack_bf16x2(sum[i][0] * inv, sum[i][1] * inv);
+      w0[2 * i + 1] = pack_bf16x2(sum[i][2] * inv, sum[i][3] * inv);
+      w1[2 * i] = pack_bf16x2(sum[i + 2][0] * inv, sum[i + 2][1] * inv);
+      w1[2 * i + 1] = pack_bf16x2(sum[i + 2][2] * inv, sum[i + 2][3] * inv);
+    }
+    *(u32x4*)orow = w0;
+    *(u32x4*)(orow + 8) = w1;
+    if (a.lse_out && wave == 0 && g == 0) a.lse_out[b * R + row.g] = lse;
+  } else {
+    const int64_t prow = slot * R + row.g;
+    float* orow = a.o_part + prow * kDc + ch;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(f32x4*)(orow + 4 * i) = sum[i] * inv;
+    if (wave == 0 && g == 0) a.lse_part[prow] = lse;
+  }
+}
+
+// Attention of sequence b over tiles [k0, k1) (32-token tiles, as
+// process_range) with independent wavefronts; <= 16 rows.
+template <int F, bool kDirect>
+__device__ __forceinline__ void process_range_iw(const DecodeArgs& a, __bf16* smem, int b, int L, int k0, int k1,
+                                                 int64_t slot, int chunk) {
+  IwRed& red = *(IwRed*)((char*)smem + kIwRedOff);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int R = a.heads;
+  const int rows = a.s_q * a.chunk_heads;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  // fused append: as process_range
+  if (a.new_latent && k1 == (L + kTileTok - 1) / kTileTok && wave == 0) {
+    const int64_t page = bt[(L - 1) / kPage];
+    if (page >= 0 && page < a.num_pages)
+      append_row<F>(a.new_latent + (int64_t)b * kDc, a.new_rope + (int64_t)b * kDr,
+                    a.append_cache + page * (int64_t)PageLayout<F>::kBytes, (L - 1) % kPage);
+    __threadfence();
+  }
+  __syncthreads();  // the previous piece (if any) has finished with LDS
+  {  // stage q of the piece's rows (zeros for rows without a head)
+    __bf16* ql = smem + kIwWaves * kVBuf;
+    for (int ci = tid; ci < 16 * (kD / 8); ci += kIwThreads) {
+      const int r = ci / (kD / 8), c = ci % (kD / 8);
+      const RowOf qrow = row_of(a, chunk, L, r);
+      bf16x8 v = {};
+      if (r < rows && qrow.valid) v = *(const bf16x8*)(a.q + ((int64_t)b * R + qrow.g) * kD + 8 * c);
+      *(bf16x8*)(ql + r * kIwQRow + 8 * c) = v;
+    }
+  }
+  __syncthreads();
+  const RowOf row = row_of(a, chunk, L, lane & 15);
+  const int limit = min(row.limit, L);
+  const int u0 = 2 * k0, u1 = min(2 * k1, (L + kSubTok - 1) / kSubTok);
+  bool fixed = false;
+  float m_fixed = 0.0f;
+  for (int pass = 0;; ++pass) {
+    IwAcc acc;
+    const bool lifted = iw_pass<F>(a, smem, bt, L, u0, u1, limit, fixed, m_fixed, acc);
+    const bool redo = __syncthreads_or(lifted);
+    float M, Ltot, seen, f_own;
+    iw_totals(red, acc, M, Ltot, seen, f_own);
+    if (!redo || pass > 0) {
+      acc.l_sum = Ltot;
+      iw_write<kDirect>(a, smem, b, slot, chunk, L, acc, M, f_own);
+      return;
+    }
+    fixed = true;
+    m_fixed = seen;
+    __syncthreads();  // every wavefront has read `red` before the next pass can rewrite it
+  }
+}
+
 // Attention of sequence b over its tiles [k0, k1) (non-empty) for the rows of
 // head chunk `chunk`, written to `slot`.  Called by every thread of the
 // workgroup (uniform control flow).
@@ -1017,8 +1523,21 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
 
 // Per-sequence splits: workgroup (split, b) covers pages [split * P, (split + 1) * P)
 // of sequence b, the last split running to the end of the sequence.
+// Threads of a decode workgroup: 512 for the independent-wavefront variant
+// (C = 0), else 256.
+template <int C> constexpr int decode_threads() { return C == 0 ? kIwThreads : kThreads; }
+
 template <int F, bool kDirect, int C>
-__global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode(const DecodeArgs a) {
+__device__ __forceinline__ void run_range(const DecodeArgs& a, __bf16* smem, int b, int L, int k0, int k1,
+                                          int64_t slot, int chunk) {
+  if constexpr (C == 0)
+    process_range_iw<F, kDirect>(a, smem, b, L, k0, k1, slot, chunk);
+  else
+    process_range<F, kDirect, C>(a, smem, b, L, k0, k1, slot, chunk);
+}
+
+template <int F, bool kDirect, int C>
+__global__ __launch_bounds__(decode_threads<C>(), C == 4 ? 2 : 1) void k_decode(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   const int split = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
   const int tid = threadIdx.x;
@@ -1029,7 +1548,7 @@ __global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode(const Decod
   const int p1 = (split == a.num_splits - 1) ? n_pages : min(p0 + a.pages_per_split, n_pages);
   if (p0 >= p1) {  // empty split: the chunk's rows get weight 0 (direct mode: output 0, lse -inf)
     const int rows = a.s_q * a.chunk_heads;
-    for (int i = tid; i < rows * (kDirect ? kDc / 8 : 1); i += kThreads) {
+    for (int i = tid; i < rows * (kDirect ? kDc / 8 : 1); i += decode_threads<C>()) {
       const RowOf row = row_of(a, chunk, L, kDirect ? i / (kDc / 8) : i);
       if (!row.valid) continue;
       if (kDirect) {
@@ -1042,8 +1561,8 @@ __global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode(const Decod
     return;
   }
   // tiles are half pages: tile k covers tokens [32 k, 32 k + 32)
-  process_range<F, kDirect, C>(a, smem, b, L, 2 * p0, min(2 * p1, (L + kTileTok - 1) / kTileTok),
-                               (int64_t)b * a.num_splits + split, chunk);
+  run_range<F, kDirect, C>(a, smem, b, L, 2 * p0, min(2 * p1, (L + kTileTok - 1) / kTileTok),
+                           (int64_t)b * a.num_splits + split, chunk);
 }
 
 // Balanced partition: the batch's pages, laid end to end in sequence order
@@ -1166,7 +1685,8 @@ __device__ __forceinline__ void flat_next_piece(const DecodeArgs& a, FlatWalk& w
 }
 
 template <int F, int C>
-__global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode_flat(const DecodeArgs a) {
+__global__ __launch_bounds__(decode_threads<C>(), C == 4 ? 2 : 1) void k_decode_flat(const DecodeArgs a) {
+  constexpr int NT = decode_threads<C>();
   extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
   __shared__ unsigned long long s_total;
   __shared__ FlatWalk walk;
@@ -1174,12 +1694,12 @@ __global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode_flat(const 
   const int64_t w = blockIdx.x;
   // one read of the lengths: the first kThreads stay in LDS for the walk
   const int len_t = tid < a.batch ? clamped_len(a, tid) : 0;
-  walk.lens[tid] = len_t;
+  if (tid < kThreads) walk.lens[tid] = len_t;
   if (tid == 0) s_total = 0;
   __syncthreads();
   {
     unsigned long long part = (len_t + kPage - 1) / kPage;
-    for (int b = tid + kThreads; b < a.batch; b += kThreads) part += (clamped_len(a, b) + kPage - 1) / kPage;
+    for (int b = tid + NT; b < a.batch; b += NT) part += (clamped_len(a, b) + kPage - 1) / kPage;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d);
     if ((tid & 63) == 0) atomicAdd(&s_total, part);
@@ -1188,7 +1708,7 @@ __global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode_flat(const 
   const int64_t T = (int64_t)uniform64(s_total);
   // empty sequences own no slots: record (0, 0) for them (strided over
   // workgroups; head chunk 0 writes all slot records)
-  for (int b = (int)w * kThreads + tid; blockIdx.y == 0 && b < a.batch; b += (int)gridDim.x * kThreads)
+  for (int b = (int)w * NT + tid; blockIdx.y == 0 && b < a.batch; b += (int)gridDim.x * NT)
     if ((b == tid ? len_t : clamped_len(a, b)) == 0) {
       a.meta[2 * b] = 0;
       a.meta[2 * b + 1] = 0;
@@ -1212,7 +1732,7 @@ __global__ __launch_bounds__(kThreads, C == 4 ? 2 : 1) void k_decode_flat(const 
     const int L = __builtin_amdgcn_readfirstlane(walk.piece[1]);
     const int k0 = __builtin_amdgcn_readfirstlane(walk.piece[2]);
     const int k1 = __builtin_amdgcn_readfirstlane(walk.piece[3]);
-    process_range<F, false, C>(a, smem, b, L, k0, k1, w + b, blockIdx.y);
+    run_range<F, false, C>(a, smem, b, L, k0, k1, w + b, blockIdx.y);
   }
 }
 
@@ -1318,32 +1838,35 @@ __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ 
 // kernel's 2112 static bytes, 80960 of the 81920 bytes each may hold).
 constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
 template <int C> constexpr size_t decode_lds() {
-  // channel split: two tiles and 4 KB of weights per head group (4 / C groups)
-  return C > 1 ? 2 * (size_t)kTile * sizeof(__bf16) + 4096 * (4 / C) : kDecodeLds;
+  // channel split: two tiles and 4 KB of weights per head group (4 / C groups);
+  // independent wavefronts: eight V buffers, q and the merge record
+  return C == 0 ? kIwLds : C > 1 ? 2 * (size_t)kTile * sizeof(__bf16) + 4096 * (4 / C) : kDecodeLds;
 }
 
 // The dynamic LDS size above 64 KB must be allowed once per kernel and device
 // (bit d of `done` records device d; setting it twice is harmless).
 template <typename K>
-static hipError_t set_lds(K kernel, std::atomic<unsigned long long>& done) {
+static hipError_t set_lds(K kernel, size_t bytes, std::atomic<unsigned long long>& done) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
   if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
-  e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLds);
+  e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e == hipSuccess) done.fetch_or(bit, std::memory_order_relaxed);
   return e;
 }
 
-// Channel split by rows per sequence for the quantized formats: all 4
-// wavefronts on one group of <= 32 rows (two workgroups per compute unit),
+// Kernel variant by rows per sequence for the quantized formats:
+// independent wavefronts at <= 16 rows (0), all 4 wavefronts on one group of
+// 17..32 rows (two workgroups per compute unit),
 // 2 wavefronts per group for 33..64 rows, else one head group per wavefront
 // (the unquantized baseline always uses the latter).  On 8 x 131072 C4R4
-// tokens, balanced: 16 heads 0.222 -> 0.167 ms, 64 heads 0.309 -> 0.283 ms.
+// tokens, balanced: 16 heads 0.222 -> 0.167 ms (channel split) -> 0.147 ms
+// (independent wavefronts), 64 heads 0.309 -> 0.283 ms.
 static int channel_split(int fmt, int rows) {
   if (fmt == kBF16) return 1;
-  return rows <= 32 ? 4 : rows <= 64 ? 2 : 1;
+  return rows <= 16 ? 0 : rows <= 32 ? 4 : rows <= 64 ? 2 : 1;
 }
 
 int workgroups_per_cu(int fmt, int rows) { return channel_split(fmt, rows) == 4 ? 2 : 1; }
@@ -1354,9 +1877,10 @@ static int head_chunks(const DecodeArgs& a) { return (a.qheads + a.chunk_heads -
 template <int F, bool D, int C>
 static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream) {
   static std::atomic<unsigned long long> attr_done{0};
-  hipError_t e = set_lds(k_decode<F, D, C>, attr_done);
+  hipError_t e = set_lds(k_decode<F, D, C>, decode_lds<C>(), attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch, head_chunks(a)), dim3(kThreads), decode_lds<C>(),
+  hipLaunchKernelGGL((k_decode<F, D, C>), dim3(a.num_splits, batch, head_chunks(a)), dim3(decode_threads<C>()),
+                     decode_lds<C>(),
                      stream, a);
   return hipGetLastError();
 }
@@ -1364,9 +1888,10 @@ static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t stream)
 template <int F, int C>
 static hipError_t launch_flat_one(const DecodeArgs& a, int groups, hipStream_t stream) {
   static std::atomic<unsigned long long> attr_done{0};
-  hipError_t e = set_lds(k_decode_flat<F, C>, attr_done);
+  hipError_t e = set_lds(k_decode_flat<F, C>, decode_lds<C>(), attr_done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups, head_chunks(a)), dim3(kThreads), decode_lds<C>(), stream, a);
+  hipLaunchKernelGGL((k_decode_flat<F, C>), dim3(groups, head_chunks(a)), dim3(decode_threads<C>()), decode_lds<C>(),
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -1378,11 +1903,13 @@ static hipError_t launch_split(bool direct, const DecodeArgs& a, int batch, hipS
 hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, hipStream_t stream) {
   const int c = channel_split(fmt, a.s_q * a.chunk_heads);
   if (fmt == kC4R4)
-    return c == 4 ? launch_split<kC4R4, 4>(direct, a, batch, stream)
+    return c == 0 ? launch_split<kC4R4, 0>(direct, a, batch, stream)
+           : c == 4 ? launch_split<kC4R4, 4>(direct, a, batch, stream)
            : c == 2 ? launch_split<kC4R4, 2>(direct, a, batch, stream)
                     : launch_split<kC4R4, 1>(direct, a, batch, stream);
   if (fmt == kC2R4)
-    return c == 4 ? launch_split<kC2R4, 4>(direct, a, batch, stream)
+    return c == 0 ? launch_split<kC2R4, 0>(direct, a, batch, stream)
+           : c == 4 ? launch_split<kC2R4, 4>(direct, a, batch, stream)
            : c == 2 ? launch_split<kC2R4, 2>(direct, a, batch, stream)
                     : launch_split<kC2R4, 1>(direct, a, batch, stream);
   return launch_split<kBF16, 1>(direct, a, batch, stream);
@@ -1391,11 +1918,13 @@ hipError_t launch_decode(int fmt, bool direct, const DecodeArgs& a, int batch, h
 hipError_t launch_decode_flat(int fmt, const DecodeArgs& a, int groups, hipStream_t stream) {
   const int c = channel_split(fmt, a.s_q * a.chunk_heads);
   if (fmt == kC4R4)
-    return c == 4 ? launch_flat_one<kC4R4, 4>(a, groups, stream)
+    return c == 0 ? launch_flat_one<kC4R4, 0>(a, groups, stream)
+           : c == 4 ? launch_flat_one<kC4R4, 4>(a, groups, stream)
            : c == 2 ? launch_flat_one<kC4R4, 2>(a, groups, stream)
                     : launch_flat_one<kC4R4, 1>(a, groups, stream);
   if (fmt == kC2R4)
-    return c == 4 ? launch_flat_one<kC2R4, 4>(a, groups, stream)
+    return c == 0 ? launch_flat_one<kC2R4, 0>(a, groups, stream)
+           : c == 4 ? launch_flat_one<kC2R4, 4>(a, groups, stream)
            : c == 2 ? launch_flat_one<kC2R4, 2>(a, groups, stream)
                     : launch_flat_one<kC2R4, 1>(a, groups, stream);
   return launch_flat_one<kBF16, 1>(a, groups, stream);

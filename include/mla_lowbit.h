@@ -112,7 +112,7 @@ mla_status_t mla_quant_append(const mla_format_t* fmt,
  * queries below describe this library's split-KV decode.)
  * A per-sequence split count suited to this shape (from the batch size, the
  * longest sequence and the workgroups the compute units hold at once: two
- * per unit for the quantized formats at <= 32 heads), for callers that want
+ * per unit for the quantized formats at 17..32 heads), for callers that want
  * the fixed-split mode; always in [1, 64].  num_splits = 0 (the balanced
  * partition) needs no such choice. */
 int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t num_heads,
@@ -125,7 +125,7 @@ int32_t mla_decode_num_splits(const mla_format_t* fmt, int32_t batch, int32_t nu
  * G + batch partial slots, then int32 [batch, 2] (first slot, slot count)
  * per sequence, where G (the balanced partition's workgroups) is the current
  * device's compute units (at most 256 are used; an MI355X has 256) times the
- * workgroups one unit holds: two for the quantized formats at <= 32 rows per
+ * workgroups one unit holds: two for the quantized formats at 17..32 rows per
  * sequence, else one (so G = 512 or 256 on an MI355X).  Each array starts
  * 256-byte aligned.  Sizes are for the device current at the call: query them
  * with the device that will run the decode current. */

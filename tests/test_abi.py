@@ -73,8 +73,9 @@ def test_split_heuristic_and_workspace():
         expect = (n * 512 * 4 + 255) // 256 * 256 + (n * 4 + 255) // 256 * 256
         assert mla.mla_decode_workspace_bytes(f, B, H, S) == expect
     # balanced partition: G + B slots, then int32 (first slot, count) per sequence; G = 512
-    # workgroups (two per compute unit) where the quantized formats split channels (<= 32 rows)
-    for fm, B, H, G in [(f, 8, 128, 256), (f, 1, 1, 512), (f, 300, 17, 512), ("C2R4", 4, 32, 512),
+    # workgroups (two per compute unit) where the quantized formats split channels (17..32 rows),
+    # else 256 (one per unit; at <= 16 rows a unit holds one 512-thread workgroup)
+    for fm, B, H, G in [(f, 8, 128, 256), (f, 1, 1, 256), (f, 4, 16, 256), (f, 300, 17, 512), ("C2R4", 4, 32, 512),
                         ("C2R4", 4, 33, 256), ("BF16", 1, 1, 256), ("BF16", 8, 128, 256)]:
         n = (G + B) * H
         expect = (n * 512 * 4 + 255) // 256 * 256 + (n * 4 + 255) // 256 * 256 + (B * 8 + 255) // 256 * 256
@@ -82,9 +83,10 @@ def test_split_heuristic_and_workspace():
         assert mla.mla_decode_partial_slots(fm, B, H, 0) == G + B
     assert mla.mla_decode_partial_slots(f, 8, 128, 32) == 256
     assert mla.mla_decode_partial_slots(f, 8, 0, 0) == 0
-    # fixed splits fill the resident workgroups: 512 at <= 32 heads
-    assert mla.mla_decode_num_splits(f, 8, 16, 131072) == 64
-    assert mla.mla_decode_num_splits(f, 16, 16, 131072) == 32
+    # fixed splits fill the resident workgroups: 512 at 17..32 heads
+    assert mla.mla_decode_num_splits(f, 8, 17, 131072) == 64
+    assert mla.mla_decode_num_splits(f, 16, 32, 131072) == 32
+    assert mla.mla_decode_num_splits(f, 8, 16, 131072) == 32
     assert mla.mla_decode_num_splits("BF16", 16, 16, 131072) == 16
     assert mla.mla_decode_workspace_bytes(f, 8, 0, 4) == 0
     assert mla.mla_decode_workspace_bytes(f, 8, 128, -1) == 0

@@ -119,6 +119,22 @@ def test_fullsize_sampled(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ["c4r4_128k", "c2r4_32k_outliers"])
+def test_fullsize_16_heads(name):
+    """The 16-head share of the full-size workloads (the bench's 16-head record):
+    sampled sequences, every head, against the oracle."""
+    w = W.derive(W.WORKLOADS[name], heads=16)
+    _say("full-size %s at 16 heads: B=%d fmt=%s" % (name, w.batch, w.fmt))
+    lens, bt, npages, cache = _build(w, w.fmt)
+    q, out, lse, S = _decode(w, w.fmt, lens, bt, cache)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    for b in sorted({0, w.batch - 1}):
+        _say("  check sequence %d (L=%d)" % (b, int(lens[b])))
+        _check_sequence(w, w.fmt, b, lens, bt, cache, q, out, lse)
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_fullsize_bf16_baseline_on_c2r4_data():
     """The unquantized-cache kernel on the C2R4 workload's data (the baseline
     the low-bit path is compared with)."""

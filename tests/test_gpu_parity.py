@@ -292,7 +292,7 @@ def test_balanced_partition_pieces(fmt, lens, heads):
     torch.cuda.synchronize()
     o_part, l_part, meta = (t.cpu().numpy() for t in mla.balanced_workspace_views(fmt, ws, B, H))
     groups = mla.mla_decode_partial_slots(fmt, B, H, 0) - B   # 512 where two workgroups share a unit
-    assert groups == (512 if fmt != "BF16" and H <= 32 else 256)
+    assert groups == (512 if fmt != "BF16" and 16 < H <= 32 else 256)
     pieces, want_meta = balanced_pieces(lens, groups)
     assert np.array_equal(meta, want_meta)
     for slot, (b, p0, p1) in sorted(pieces.items()):
@@ -383,11 +383,12 @@ def test_fused_append_decode_equals_separate(fmt, splits, heads):
 
 
 @pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "BF16"])
-@pytest.mark.parametrize("s_q,heads", [(2, 64), (4, 8), (2, 24), (3, 100), (16, 16)])
+@pytest.mark.parametrize("s_q,heads", [(2, 64), (4, 8), (2, 24), (3, 100), (16, 16), (2, 8), (3, 5)])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_multi_token_decode(fmt, s_q, heads, splits):
     """Several query tokens per sequence (causal among themselves): 128 rows in
-    one workgroup, 32 rows (channel split), and rows split into head chunks;
+    one workgroup, 32 rows (channel split), <= 16 rows (independent wavefronts),
+    and rows split into head chunks;
     a sequence shorter than the query count; against oracle.decode_multi."""
     _say("multi-token %s s_q=%d H=%d S=%d" % (fmt, s_q, heads, splits))
     lens = [1500, 3, 70, 0, 64, 333]
