@@ -12,8 +12,8 @@
 // sequence the wavefronts of a head group split its channels instead (four
 // per group at 17..32 rows, two workgroups per compute unit; two per group at
 // 33..64 rows), sharing one softmax through LDS, see split_pass_cs; at <= 16
-// rows (quantized formats) eight independent wavefronts each carry their own
-// 16-token sub-tiles, see process_range_iw.  The work
+// rows (quantized formats) the four wavefronts work independently, each on
+// its own 32-token tiles, see process_range_iw.  The work
 // is tiled by half pages (32 tokens):
 //   1. fill: every thread loads its share of the next tile's packed bytes
 //      (16-byte loads; the 32 lanes of a half-wave read 512 contiguous bytes of
@@ -892,42 +892,45 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t 
 
 // ---------------------------------------------------------------- independent wavefronts (<= 16 rows)
 // At <= 16 rows per sequence one 16 x 16 MFMA block holds every row, so a
-// wavefront can carry 16 tokens through the whole attention step on its own.
-// Eight wavefronts per workgroup (two per SIMD, one workgroup per compute
-// unit) take every eighth 16-token sub-tile of the piece, each:
-//   1. loads the packed bytes of its next sub-tile while this one computes;
-//      lane (t, g) = (lane % 16, lane / 16) owns token t of the sub-tile and
-//      a quarter of its channels: the 8 values of k-step ks that Q.K^T needs
-//      in its lane (channels chan(ks, g) .. + 8) are one code dword;
+// wavefront can carry its own tokens through the whole attention step.  Four
+// wavefronts per workgroup (one per SIMD, one workgroup per compute unit)
+// take every fourth 32-token tile of the piece; a tile is two 16-token
+// blocks b = 0, 1.  Each wavefront, per tile:
+//   1. loads the tile's packed bytes while the previous tile computes; lane
+//      (t, g) = (lane % 16, lane / 16) owns token t of both blocks and a
+//      quarter of their channels: the 8 values of k-step ks that Q.K^T needs
+//      in its lane (channels iw_chan(ks, g) .. + 8) are one code dword;
 //   2. dequantizes k-step by k-step in registers, straight into the A operand
-//      of MFMA 16x16x32 bf16 (16 tokens x 32 channels), B = q^T read from LDS
-//      (the rows of the piece are staged once per piece); the content values
-//      also go to the wavefront's own LDS buffer for step 4.  Output: S^T, lane
-//      (h, g) holding row h for tokens 4 g .. 4 g + 3;
-//   3. takes the four softmax weights of its lane against a fixed reference
-//      per wavefront and pass (as in split_pass), splits them into high and
-//      low bf16 halves, and trades halves with lane l ^ 32 (one
-//      v_permlane32_swap per pair) so that lanes 0..31 hold the high halves of
-//      16 tokens and lanes 32..63 the low halves;
-//   4. P.V on MFMA 16x16x32 bf16 with k = 16 tokens x {high, low}: A = V^T
-//      (16 channels x the same 16 tokens twice) from transposing LDS reads of
-//      its buffer, O^T (512 channels x 16 rows) in 32 x 4 accumulators.
-// No barrier is taken per sub-tile: while one wavefront of a SIMD
-// dequantizes, the other's MFMAs run.  At the end of a piece the eight
+//      of MFMA 16x16x32 bf16 (16 tokens x 32 channels), one MFMA per block
+//      sharing B = q^T read from LDS (the rows of the piece are staged once
+//      per piece); the content values also go to the wavefront's own LDS
+//      buffer for step 4.  Output: S^T, lane (h, g) holding row h for tokens
+//      4 g .. 4 g + 3 of each block;
+//   3. takes the eight softmax weights of its lane against a fixed reference
+//      per wavefront and pass (as in split_pass) and splits them into high
+//      and low bf16 halves: the lane's weights are already its slots of the
+//      P.V operand (k slots 0..3: block 0 tokens 4 g + [0, 4), slots 4..7: block
+//      1 tokens 4 g + [0, 4));
+//   4. P.V on MFMA 16x16x32 bf16 with k = the tile's 32 tokens: A = V^T (16
+//      channels x 32 tokens) from two transposing LDS reads of its buffer,
+//      one MFMA with the high and one with the low weights, O^T (512 channels
+//      x 16 rows) in 32 x 4 accumulators.
+// Software pipelining: the P.V of tile i runs between the Q.K^T k-steps of
+// tile i + 1.  No barrier is taken per tile.  At the end of a piece the four
 // partial results (each against its own reference) are merged through LDS
 // with log-sum-exp weights.
-constexpr int kIwWaves = 8;
+constexpr int kIwWaves = 4;
 constexpr int kIwThreads = 64 * kIwWaves;
-constexpr int kSubTok = 16;                       // tokens per sub-tile
+constexpr int kIwTok = 32;                        // tokens per tile of a wavefront
 constexpr int kVRow = kDc + 16;                   // bf16 per row of a V buffer (1056 bytes; see vrow)
-constexpr int kVBuf = kSubTok * kVRow;            // bf16 per wavefront buffer
+constexpr int kVBuf = kIwTok * kVRow;             // bf16 per wavefront buffer
 constexpr int kIwQRow = kD + 8;                   // bf16 per staged q row (1168 bytes)
 constexpr int kIwRedRow = kDc + 4;                // fp32 per row in the end-of-piece merge
-constexpr size_t kIwRedOff = ((size_t)kIwWaves * kVBuf + 16 * kIwQRow) * sizeof(__bf16);  // 151808 bytes
-static_assert(4 * 16 * kIwRedRow * sizeof(float) <= (size_t)kIwWaves * kVBuf * sizeof(__bf16),
-              "four wavefronts' outputs fit in the V buffers");
+constexpr size_t kIwRedOff = ((size_t)kIwWaves * kVBuf + 16 * kIwQRow) * sizeof(__bf16);  // 153856 bytes
+static_assert(kIwWaves * 16 * kIwRedRow * sizeof(float) <= (size_t)kIwWaves * kVBuf * sizeof(__bf16),
+              "the wavefronts' outputs fit in the V buffers");
 
-// value of lane l ^ 16 / l ^ 32 (through ds_bpermute; used once per pass)
+// value of lane l ^ 16 / l ^ 32 (through ds_bpermute; used a few times per pass)
 __device__ __forceinline__ float lane_xor(float v, int m) {
   return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), m));
 }
@@ -956,17 +959,17 @@ __device__ __forceinline__ bf16x8 dq_int2x8(const unsigned (&b)[4], int hf, floa
   return __builtin_bit_cast(bf16x8, o);
 }
 
-// Packed bytes of one lane's share of a sub-tile (token t of the page, lane
-// group g) and the dequantization of its k-steps.  Both formats give lane
-// group g the same channels: content k-step ks = 4 m + d (block m = 128
+// Packed bytes of one lane's share of a 16-token block (token t of the block,
+// lane group g) and the dequantization of its k-steps.  Both formats give
+// lane group g the same channels: content k-step ks = 4 m + d (block m of 128
 // channels) holds channels 128 m + 32 g + 8 d .. + 8 of the lane's token, and
-// RoPE k-steps 16, 17 hold channels 512 + 32 (ks - 16) + 8 g .. + 8 (chan()).
-// The q operand and the V buffer use the same offsets.  The registers hold
-// one sub-tile: part i (content block m = i, or the RoPE part i = 4) is
-// reloaded with the next sub-tile's bytes right after its last k-step, so
-// the loads of the next sub-tile are in flight while this one computes.
+// RoPE k-steps 16, 17 hold channels 512 + 32 (ks - 16) + 8 g .. + 8
+// (iw_chan).  The q operand and the V buffer use the same offsets.  The
+// registers hold one block: part i (content block m = i, or the RoPE part
+// i = 4) is reloaded with the next tile's bytes right after its last k-step,
+// so the loads of the next tile are in flight while this one computes.
 // Addresses: a wavefront-uniform page base plus per-lane offsets fixed for
-// the pass.
+// the pass; `hp` is the block's quarter of its page.
 __device__ __forceinline__ constexpr int iw_chan(int ks, int g) {
   return ks < 16 ? 128 * (ks >> 2) + 32 * g + 8 * (ks & 3) : kDc + 32 * (ks - 16) + 8 * g;
 }
@@ -987,9 +990,7 @@ template <> struct SubFill<kC4R4> {
   unsigned sz[4];
   unsigned r[2];    // dword g of RoPE chunks 0, 1
   unsigned rsz;
-  const uint8_t* pb;  // page base of the sub-tile whose bytes issue() loads
-  int hp;             // its quarter of the page
-  __device__ __forceinline__ void issue(int i, const SubLanes& o) {
+  __device__ __forceinline__ void issue(int i, const uint8_t* pb, int hp, const SubLanes& o) {
     if (i < 4) {
       c[i] = *(const u32x4*)(pb + Lay::kCodesA + 256 * hp + 4096 * i + o.c);
       sz[i] = *(const unsigned*)(pb + Lay::kSzB + 64 * hp + 512 * i + o.sz);
@@ -1019,9 +1020,7 @@ template <> struct SubFill<kC2R4> {
   unsigned r[2];
   unsigned rsz;
   unsigned b[4];    // masked code bytes of the dword being converted
-  const uint8_t* pb;
-  int hp;
-  __device__ __forceinline__ void issue(int i, const SubLanes& o) {
+  __device__ __forceinline__ void issue(int i, const uint8_t* pb, int hp, const SubLanes& o) {
     if (i < 4) {
       c[i] = *(const u32x2*)(pb + Lay::kCodesA + 256 * hp + 2048 * i + o.c);
       sz[i] = *(const unsigned*)(pb + Lay::kSzB + 64 * hp + 1024 * i + o.sz);
@@ -1046,28 +1045,6 @@ template <> struct SubFill<kC2R4> {
   }
 };
 
-// Block-table window over sub-tiles (4 per page), as PageWindow.
-struct SubPageWindow {
-  const int32_t* bt;
-  int p_end, wbase, ids;
-  __device__ __forceinline__ SubPageWindow(const int32_t* bt_, int u0, int u1) : bt(bt_) {
-    p_end = (u1 + 3) >> 2;
-    wbase = u0 >> 2;
-    const int lane = threadIdx.x & 63;
-    ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
-  }
-  __device__ __forceinline__ int page_of(int u) {
-    const int pg = u >> 2;
-    if (pg - wbase >= 64) {  // uniform per wavefront; every 64 pages
-      wbase = pg;
-      const int lane = threadIdx.x & 63;
-      ids = wbase + lane < p_end ? bt[wbase + lane] : -1;
-      return __builtin_amdgcn_readlane(ids, 0);
-    }
-    return __builtin_amdgcn_readlane(ids, pg - wbase);
-  }
-};
-
 struct IwAcc {
   f32x4 o[32];   // o[ct][r]: O^T[16 ct + 4 g + r][lane's row], against 2^m_ref
   float l_sum;   // this lane's tokens' share of sum_t p_t
@@ -1075,25 +1052,28 @@ struct IwAcc {
   float m_seen;  // max logit (log2 units) of this lane's tokens
 };
 
-// Row t of a wavefront's V buffer starts at element vrow(t): rows 528 bf16
-// (1056 bytes) apart, rows 8..15 shifted by 16 bytes.
-__device__ __forceinline__ constexpr int vrow(int t) { return t * kVRow + 8 * (t >> 3); }
+// Row r of a wavefront's V buffer (token r of the tile) starts at element
+// vrow(r): rows 528 bf16 (1056 bytes) apart, rows 8..15 and 24..31 shifted by
+// 16 bytes, so that the rows a 16-byte write touches (16 tokens of a block)
+// and the rows a transposing read touches (8 tokens per 32 lanes) fall on
+// distinct LDS banks.
+__device__ __forceinline__ constexpr int vrow(int r) { return r * kVRow + 8 * ((r >> 3) & 1); }
 
 // Q.K^T k-step order: the RoPE k-steps first (they write no V), then the
 // content blocks in channel order.
 __device__ __forceinline__ constexpr int iw_ks(int p) { return p < 2 ? 16 + p : p - 2; }
-// P.V channel tiles issued with Q.K^T step p of the next sub-tile: 4 each
-// with the RoPE steps (block 0), then 2 per content step of blocks 0..2 (the
-// tiles of block m + 1), none during block 3.  Every tile of block m is read
-// before step 2 + 4 m writes block m of the next sub-tile.
+// P.V channel tiles issued with Q.K^T step p of the next tile: 4 each with
+// the RoPE steps (channel block 0), then 2 per content step of channel
+// blocks 0..2 (the tiles of block m + 1), none during block 3.  Every tile of
+// channel block m is read before step 2 + 4 m writes block m of the next tile.
 __device__ __forceinline__ constexpr int pv_begin(int p) { return p < 2 ? 4 * p : p < 14 ? 8 + 2 * (p - 2) : 32; }
 __device__ __forceinline__ constexpr int pv_end(int p) { return p < 2 ? 4 * p + 4 : p < 14 ? 10 + 2 * (p - 2) : 32; }
 
-// One pass of wavefront `wave` over its sub-tiles u0 + wave + 8 i < u1 of the
-// piece, software-pipelined: the P.V of sub-tile i runs between the Q.K^T
-// k-steps (dequantization, MFMA) of sub-tile i + 1.  Returns true if a
-// weight may have overflowed (a logit more than kMaxLift above the
-// reference): the caller redoes the piece with a fixed reference.
+// One pass of wavefront `wave` over its tiles u0 + wave + 4 i < u1 of the
+// piece (32-token tiles), software-pipelined: the P.V of tile i runs between
+// the Q.K^T k-steps of tile i + 1.  Returns true if a weight may have
+// overflowed (a logit more than kMaxLift above the reference): the caller
+// redoes the piece with a fixed reference.
 template <int F>
 __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int u0, int u1,
                                         int limit, bool fixed, float m_fixed, IwAcc& acc) {
@@ -1112,41 +1092,48 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   bool first = !fixed;
   const int ufirst = u0 + wave;
   if (ufirst >= u1) return false;
-  SubPageWindow win(bt, ufirst, u1);
-  // transposing-read addresses of the P.V operand: block kg = lane / 16 reads
-  // tokens 4 (kg & 1) + j (then + 8), lane 4 j + r of the block channels
-  // 4 r .. + 4 of the channel tile; lane i of the block receives channel i of
-  // those 4 tokens
-  const int tr_tok = 4 * (g & 1) + ((lane & 15) >> 2);
-  const __bf16* __restrict__ vtr = vbuf + vrow(tr_tok) + 4 * (lane & 3);
+  PageWindow win(bt, ufirst, u1);
+  // transposing-read addresses of the P.V operand: lane block kg = lane / 16
+  // reads tokens 4 kg + j of block 0 (then of block 1), lane 4 j + r of the
+  // block channels 4 r .. + 4 of the channel tile; lane i of the block
+  // receives channel i of those 4 tokens
+  const __bf16* __restrict__ vtr = vbuf + vrow(4 * g + ((lane & 15) >> 2)) + 4 * (lane & 3);
   auto tr_read = [&](int ct) {
     const __bf16* v0 = vtr + 16 * ct;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v0);
-    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + vrow(8)));
+    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + vrow(16)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  __bf16* __restrict__ vw = vbuf + vrow(t);
+  __bf16* __restrict__ vw0 = vbuf + vrow(t);
+  __bf16* __restrict__ vw1 = vbuf + vrow(16 + t);
   const SubLanes lo = SF::lanes(t, g);
 
-  SF f;
+  SF f0, f1;  // blocks 0 and 1 of the tile
+  const uint8_t* pb = nullptr;
+  int hpt = 0;   // half of the page of the tile whose bytes issue() loads next
   int pg_next = win.page_of(ufirst);
-  auto aim = [&](int page, int u) {  // the sub-tile whose bytes issue() loads next
+  auto aim = [&](int page, int u) {
     const bool ok = page >= 0 && page < a.num_pages;
-    f.pb = a.cache + (ok ? page : 0) * (int64_t)PageLayout<F>::kBytes;  // an invalid page reads page 0, zeroed
-    f.hp = u & 3;
+    pb = a.cache + (ok ? page : 0) * (int64_t)PageLayout<F>::kBytes;  // an invalid page reads page 0, zeroed
+    hpt = u & 1;
+  };
+  auto issue = [&](int i) {
+    f0.issue(i, pb, 2 * hpt, lo);
+    f1.issue(i, pb, 2 * hpt + 1, lo);
   };
   aim(pg_next, ufirst);
 #pragma unroll
-  for (int i = 0; i < 5; ++i) f.issue(i, lo);
+  for (int i = 0; i < 5; ++i) issue(i);
 
-  // ---- Q.K^T state of the sub-tile being dequantized
+  // ---- Q.K^T state of the tile being dequantized
   f32x4 s0, s1;
   bf16x8 qv[4];
-  float S = 0.0f, Z = 0.0f;
-  bool live = false;
+  float S0 = 0.0f, Z0 = 0.0f, S1 = 0.0f, Z1 = 0.0f;
+  bool live0 = false, live1 = false;
   auto qk_begin = [&](int u) {
-    const int pg = pg_next;
-    live = pg >= 0 && pg < a.num_pages && kSubTok * u + t < L;
+    const bool ok = pg_next >= 0 && pg_next < a.num_pages;
+    live0 = ok && kIwTok * u + t < L;
+    live1 = ok && kIwTok * u + 16 + t < L;
     const int un = u + kIwWaves < u1 ? u + kIwWaves : u;  // the last one reloads itself: harmless
     pg_next = win.page_of(un);
     aim(pg_next, un);
@@ -1157,31 +1144,40 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   };
   auto qk_step = [&](int p) {
     const int ks = iw_ks(p);
-    if (ks % 4 == 0 || ks == 16) sz_unpack(f.sz_of(ks, live), S, Z);
-    const bf16x8 kv = f.step(ks, S, Z);
+    if (ks % 4 == 0 || ks == 16) {
+      sz_unpack(f0.sz_of(ks, live0), S0, Z0);
+      sz_unpack(f1.sz_of(ks, live1), S1, Z1);
+    }
+    const bf16x8 k0 = f0.step(ks, S0, Z0);
+    const bf16x8 k1 = f1.step(ks, S1, Z1);
     const bf16x8 qk = qv[p & 3];
     if (p + 4 < 18) qv[p & 3] = *(const bf16x8*)(qlds + iw_chan(iw_ks(p + 4), g));
-    if (ks < 16) *(bf16x8*)(vw + iw_chan(ks, g)) = kv;
-    if (p & 1)
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qk, s1, 0, 0, 0);
-    else
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qk, s0, 0, 0, 0);
-    if (p == 1) f.issue(4, lo);                           // RoPE part consumed
-    if (p >= 2 && (ks & 3) == 3) f.issue(ks >> 2, lo);     // content block consumed
+    if (ks < 16) {
+      *(bf16x8*)(vw0 + iw_chan(ks, g)) = k0;
+      *(bf16x8*)(vw1 + iw_chan(ks, g)) = k1;
+    }
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qk, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qk, s1, 0, 0, 0);
+    if (p == 1) issue(4);                              // RoPE part consumed
+    if (p >= 2 && (ks & 3) == 3) issue(ks >> 2);       // content block consumed
   };
   // ---- softmax of a finished Q.K^T: weights against the reference, high /
-  //      low bf16 halves exchanged with lane l ^ 32 into the P.V operand
-  bf16x8 bp;
+  //      low bf16 halves, already in the lane's slots of the P.V operand
+  bf16x8 bph, bpl;
   auto softmax = [&](int u) {
-    f32x4 s = s0 + s1;
-    if (kSubTok * (u + 1) > limit_min) {  // the tokens past the row's limit (and the sequence end)
-      const int lt = limit - kSubTok * u - 4 * g;
+    f32x4 s[2] = {s0, s1};
+    if (kIwTok * (u + 1) > limit_min) {  // the tokens past the row's limit (and the sequence end)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r >= lt) s[r] = -INFINITY;
+      for (int b = 0; b < 2; ++b) {
+        const int lt = limit - kIwTok * u - 16 * b - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (r >= lt) s[b][r] = -INFINITY;
+      }
     }
-    const float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if (first) {  // this wavefront's reference: its first sub-tile's max (over the 16 tokens), lifted
+    const float smax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    if (first) {  // this wavefront's reference: its first tile's max (over the 32 tokens), lifted
       float m = fmaxf(smax, lane_xor(smax, 16));
       m = fmaxf(m, lane_xor(m, 32));
       acc.m_ref = finite_ref(m * a.scale_log2 + kRefLift);
@@ -1193,41 +1189,44 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
       lifted |= mt - acc.m_ref > kMaxLift;
     }
     const float neg_ref = -acc.m_ref;
-    float p[4];
+    unsigned hw[4], lw[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, neg_ref));
-    acc.l_sum += (p[0] + p[1]) + (p[2] + p[3]);
-    const unsigned h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
-    const unsigned l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-    const unsigned l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-    // lanes < 32 receive the high halves of lane l + 32, lanes >= 32 the low halves of lane l - 32
-    const auto x01 = __builtin_amdgcn_permlane32_swap(h01, l01, false, false);
-    const auto x23 = __builtin_amdgcn_permlane32_swap(h23, l23, false, false);
-    // k slots 0..3: tokens 4 (g & 1) + [0, 4), slots 4..7: those + 8; high
-    // halves in lanes 0..31, low halves in lanes 32..63
-    const u32x4 bw = lane < 32 ? (u32x4){h01, h23, x01[1], x23[1]} : (u32x4){x01[0], x23[0], l01, l23};
-    bp = __builtin_bit_cast(bf16x8, bw);
+    for (int b = 0; b < 2; ++b) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.scale_log2, neg_ref));
+      acc.l_sum += (p[0] + p[1]) + (p[2] + p[3]);
+      hw[2 * b] = pack_bf16x2(p[0], p[1]);
+      hw[2 * b + 1] = pack_bf16x2(p[2], p[3]);
+      lw[2 * b] = pack_bf16x2(p[0] - bf16_lo(hw[2 * b]), p[1] - bf16_hi(hw[2 * b]));
+      lw[2 * b + 1] = pack_bf16x2(p[2] - bf16_lo(hw[2 * b + 1]), p[3] - bf16_hi(hw[2 * b + 1]));
+    }
+    bph = __builtin_bit_cast(bf16x8, (u32x4){hw[0], hw[1], hw[2], hw[3]});
+    bpl = __builtin_bit_cast(bf16x8, (u32x4){lw[0], lw[1], lw[2], lw[3]});
   };
-  // ---- P.V of the previous sub-tile: O^T += V^T . [P_hi; P_lo], channel
-  //      tile ct, operands read 4 tiles ahead
+  // ---- P.V of the previous tile: O^T += V^T . P_hi + V^T . P_lo, channel
+  //      tile ct; operands read 3 tiles ahead, the low-weight MFMA of a tile
+  //      issued after the high one of the next (no back-to-back accumulator)
   bf16x8 va[5];
   auto pv_start = [&]() {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) va[d] = tr_read(d);
+    for (int d = 0; d < 3; ++d) va[d] = tr_read(d);
   };
   auto pv_tile = [&](int ct) {
-    if (ct + 4 < 32) va[(ct + 4) % 5] = tr_read(ct + 4);
-    acc.o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct % 5], bp, acc.o[ct], 0, 0, 0);
+    if (ct + 3 < 32) va[(ct + 3) % 5] = tr_read(ct + 3);
+    acc.o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct % 5], bph, acc.o[ct], 0, 0, 0);
+    if (ct > 0) acc.o[ct - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[(ct - 1) % 5], bpl, acc.o[ct - 1], 0, 0, 0);
+    if (ct == 31) acc.o[31] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[31 % 5], bpl, acc.o[31], 0, 0, 0);
   };
 
-  // prologue: Q.K^T and weights of the first sub-tile
+  // prologue: Q.K^T and weights of the first tile
   qk_begin(ufirst);
 #pragma unroll
   for (int p = 0; p < 18; ++p) qk_step(p);
   softmax(ufirst);
   int u = ufirst;
   for (; u + kIwWaves < u1; u += kIwWaves) {
-    // P.V of sub-tile u interleaved with Q.K^T of sub-tile u + 8
+    // P.V of tile u interleaved with Q.K^T of tile u + 4
     qk_begin(u + kIwWaves);
     pv_start();
 #pragma unroll
@@ -1238,7 +1237,7 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
     }
     softmax(u + kIwWaves);
   }
-  // epilogue: P.V of the last sub-tile
+  // epilogue: P.V of the last tile
   pv_start();
 #pragma unroll
   for (int ct = 0; ct < 32; ++ct) pv_tile(ct);
@@ -1248,8 +1247,7 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
 // Merged result of a piece for the wavefronts' rows, written to `slot`
 // (partials) or to the output (direct mode).  Per-wavefront reference,
 // denominator and seen maximum come through `red`; the O blocks through the
-// V buffers in two rounds of four wavefronts, each wavefront summing 64 of
-// the 512 channels.
+// V buffers, each wavefront summing 128 of the 512 channels.
 struct IwRed {
   float m[kIwWaves][16], l[kIwWaves][16], s[kIwWaves][16];
 };
@@ -1293,24 +1291,21 @@ template <bool kDirect>
 __device__ __forceinline__ void iw_write(const DecodeArgs& a, __bf16* smem, int b, int64_t slot, int chunk, int L,
                                          IwAcc& acc, float M, float f_own) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t = lane & 15, g = lane >> 4;
-  float* red = (float*)smem;  // 4 x [16 rows][kIwRedRow] fp32 over the V buffers
-  // this lane's summing share: row t, channels 64 wave + 16 g .. + 16
-  f32x4 sum[4] = {};
+  float* red = (float*)smem;  // kIwWaves x [16 rows][kIwRedRow] fp32 over the V buffers
+  __syncthreads();            // the V buffers are free
+  {
+    float* dst = red + wave * 16 * kIwRedRow + t * kIwRedRow + 4 * g;
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    __syncthreads();  // the V buffers are free (round 0) / read (round 1)
-    if ((wave >> 2) == round) {
-      float* dst = red + (wave & 3) * 16 * kIwRedRow + t * kIwRedRow + 4 * g;
+    for (int ct = 0; ct < 32; ++ct) *(f32x4*)(dst + 16 * ct) = acc.o[ct] * f_own;
+  }
+  __syncthreads();
+  // this lane's summing share: row t, channels 128 wave + 32 g .. + 32
+  f32x4 sum[8] = {};
 #pragma unroll
-      for (int ct = 0; ct < 32; ++ct) *(f32x4*)(dst + 16 * ct) = acc.o[ct] * f_own;
-    }
-    __syncthreads();
+  for (int src = 0; src < kIwWaves; ++src) {
+    const float* s = red + src * 16 * kIwRedRow + t * kIwRedRow + 128 * wave + 32 * g;
 #pragma unroll
-    for (int src = 0; src < 4; ++src) {
-      const float* s = red + src * 16 * kIwRedRow + t * kIwRedRow + 64 * wave + 16 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum[i] += *(const f32x4*)(s + 4 * i);
-    }
+    for (int i = 0; i < 8; ++i) sum[i] += *(const f32x4*)(s + 4 * i);
   }
   // row t of the workgroup: the totals are per row (any lane of row t holds them)
   const RowOf row = row_of(a, chunk, L, t);
@@ -1319,25 +1314,23 @@ __device__ __forceinline__ void iw_write(const DecodeArgs& a, __bf16* smem, int 
   const float inv = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
   const float lse = Ltot > 0.0f ? (M + __log2f(Ltot)) * 0.69314718055994531f : -INFINITY;
   const int R = a.heads;
-  const int ch = 64 * wave + 16 * g;
+  const int ch = 128 * wave + 32 * g;
   if (kDirect) {
     __bf16* orow = a.out + ((int64_t)b * R + row.g) * kDc + ch;
-    u32x4 w0, w1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      w0[2 * i] = pack_bf16x2(sum[i][0] * inv, sum[i][1] * inv);
-      w0[2 * i + 1] = pack_bf16x2(sum[i][2] * inv, sum[i][3] * inv);
-      w1[2 * i] = pack_bf16x2(sum[i + 2][0] * inv, sum[i + 2][1] * inv);
-      w1[2 * i + 1] = pack_bf16x2(sum[i + 2][2] * inv, sum[i + 2][3] * inv);
+    for (int j = 0; j < 4; ++j) {
+      const u32x2 w = {pack_bf16x2(sum[2 * j][0] * inv, sum[2 * j][1] * inv),
+                       pack_bf16x2(sum[2 * j][2] * inv, sum[2 * j][3] * inv)};
+      const u32x2 x = {pack_bf16x2(sum[2 * j + 1][0] * inv, sum[2 * j + 1][1] * inv),
+                       pack_bf16x2(sum[2 * j + 1][2] * inv, sum[2 * j + 1][3] * inv)};
+      *(u32x4*)(orow + 8 * j) = (u32x4){w[0], w[1], x[0], x[1]};
     }
-    *(u32x4*)orow = w0;
-    *(u32x4*)(orow + 8) = w1;
     if (a.lse_out && wave == 0 && g == 0) a.lse_out[b * R + row.g] = lse;
   } else {
     const int64_t prow = slot * R + row.g;
     float* orow = a.o_part + prow * kDc + ch;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(f32x4*)(orow + 4 * i) = sum[i] * inv;
+    for (int i = 0; i < 8; ++i) *(f32x4*)(orow + 4 * i) = sum[i] * inv;
     if (wave == 0 && g == 0) a.lse_part[prow] = lse;
   }
 }
@@ -1374,12 +1367,12 @@ __device__ __forceinline__ void process_range_iw(const DecodeArgs& a, __bf16* sm
   __syncthreads();
   const RowOf row = row_of(a, chunk, L, lane & 15);
   const int limit = min(row.limit, L);
-  const int u0 = 2 * k0, u1 = min(2 * k1, (L + kSubTok - 1) / kSubTok);
+  const int u1 = min(k1, (L + kIwTok - 1) / kIwTok);
   bool fixed = false;
   float m_fixed = 0.0f;
   for (int pass = 0;; ++pass) {
     IwAcc acc;
-    const bool lifted = iw_pass<F>(a, smem, bt, L, u0, u1, limit, fixed, m_fixed, acc);
+    const bool lifted = iw_pass<F>(a, smem, bt, L, k0, u1, limit, fixed, m_fixed, acc);
     const bool redo = __syncthreads_or(lifted);
     float M, Ltot, seen, f_own;
     iw_totals(red, acc, M, Ltot, seen, f_own);
@@ -1862,7 +1855,7 @@ static hipError_t set_lds(K kernel, size_t bytes, std::atomic<unsigned long long
 // 17..32 rows (two workgroups per compute unit),
 // 2 wavefronts per group for 33..64 rows, else one head group per wavefront
 // (the unquantized baseline always uses the latter).  On 8 x 131072 C4R4
-// tokens, balanced: 16 heads 0.222 -> 0.167 ms (channel split) -> 0.147 ms
+// tokens, balanced: 16 heads 0.222 -> 0.167 ms (channel split) -> 0.146 ms
 // (independent wavefronts), 64 heads 0.309 -> 0.283 ms.
 static int channel_split(int fmt, int rows) {
   if (fmt == kBF16) return 1;
