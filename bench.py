@@ -86,12 +86,23 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
-def counted_traffic(workload, fmt):
+def traffic_tag(workload, fmt_override="", heads_override=0):
+    """Name of a decode launch's traffic summary: the workload, then the cache
+    format if it is not the workload's own, then the head count if not its own."""
+    tag = workload
+    if fmt_override:
+        tag += "_" + fmt_override.lower()
+    if heads_override:
+        tag += "_h%d" % heads_override
+    return tag
+
+
+def counted_traffic(tag, fmt=None):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary of this workload, or None when there is none or the kernel sources have
-    changed since the counters were taken."""
+    summary `profiles/traffic_k_decode_flat_<tag>.md`, or None when there is none or
+    the kernel sources have changed since the counters were taken."""
     import re
-    path = os.path.join(ROOT, "profiles", "traffic_k_decode_flat_%s.md" % workload)
+    path = os.path.join(ROOT, "profiles", "traffic_k_decode_flat_%s.md" % tag)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -149,7 +160,7 @@ def cpu_baseline(w, seqs=8):
                               "sample": "%d tokens of one sequence, all heads, %.2f s" % (n1, dt1)}}
 
 
-def time_case(w, args, fused, S, dev, label=None):
+def time_case(w, args, fused, S, dev, label=None, tag=None):
     """Build `w`'s caches on the GPU and time the decode step on them: returns
     the step time, the decode kernel's average time (HIP events on its stream),
     packed GB/s and the kernel's roofline block."""
@@ -219,7 +230,8 @@ def time_case(w, args, fused, S, dev, label=None):
     roofline = {"kernel": ("k_decode_flat (balanced split-KV partial" if S == 0 else "k_decode (split-KV partial") +
                           (", fused append)" if fused else ")"),
                 "bound": bound, "achieved": round(achieved, 2),
-                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": counted_traffic(tag) if (tag and S == 0 and fused) else None,
                 "kernel_ms": round(k_ms, 4), "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
                 "intensity_flop_per_byte": round(intensity, 1),
                 "kernel_packed_gbs": round(k_gbs, 2), "kernel_hbm_peak_frac": round(k_gbs / HBM_PEAK_GBS, 4)}
@@ -274,26 +286,30 @@ def main():
     if args.format:
         w = W.derive(w, fmt=args.format)
     S = args.splits
-    head = time_case(w, args, not args.unfused, S, dev)
+    head = time_case(w, args, not args.unfused, S, dev,
+                     tag=traffic_tag(args.workload, args.format, args.heads))
     roofline = head["roofline"]
-    if S == 0 and not args.heads and not args.format and not args.unfused:
-        roofline["traffic"] = counted_traffic(w.name, w.fmt)
 
     # the other formats the metric names, each with its own roofline block:
     # C2R4 on its 64 x 32768 workload (5% outlier channels), the unquantized
     # BF16 cache on the same data (the in-house baseline kernel), BF16 on the
-    # headline's data, and the 16-head share of the headline cache (the
-    # HBM-bound regime of a head-sharded deployment)
+    # headline's data, the 16-head share of the headline cache (the HBM-bound
+    # regime of a head-sharded deployment) and the mixed C2R4 serving step
+    # (128 sequences of 1K-128K tokens on random pages, one token appended each)
     extra = {}
     if not args.no_extra and not args.heads and not args.format and args.workload == "c4r4_128k":
         c2 = W.WORKLOADS["c2r4_32k_outliers"]
-        extra["c2r4_32k_outliers"] = time_case(c2, args, not args.unfused, S, dev)
+        extra["c2r4_32k_outliers"] = time_case(c2, args, not args.unfused, S, dev,
+                                               tag=traffic_tag("c2r4_32k_outliers"))
         extra["bf16_on_c2r4_32k_outliers"] = time_case(W.derive(c2, fmt="BF16"), args, not args.unfused, S, dev,
-                                                       label="bf16 cache, c2r4_32k_outliers data")
+                                                       label="bf16 cache, c2r4_32k_outliers data",
+                                                       tag=traffic_tag("c2r4_32k_outliers", "BF16"))
         extra["bf16_on_c4r4_128k"] = time_case(W.derive(w, fmt="BF16"), args, not args.unfused, S, dev,
-                                               label="bf16 cache, c4r4_128k data")
+                                               label="bf16 cache, c4r4_128k data", tag=traffic_tag(w.name, "BF16"))
         extra["c4r4_128k_16_heads"] = time_case(W.derive(w, heads=16), args, not args.unfused, S, dev,
-                                                label="c4r4_128k, 16 heads")
+                                                label="c4r4_128k, 16 heads", tag=traffic_tag(w.name, "", 16))
+        extra["mixed_c2r4_serving"] = time_case(W.WORKLOADS["mixed_c2r4_serving"], args, not args.unfused, S, dev,
+                                                tag=traffic_tag("mixed_c2r4_serving"))
         for lo, bf in (("c2r4_32k_outliers", "bf16_on_c2r4_32k_outliers"), (None, "bf16_on_c4r4_128k")):
             lo_ms = extra[lo]["roofline"]["kernel_ms"] if lo else roofline["kernel_ms"]
             lo_step = extra[lo]["ms_per_step"] if lo else head["ms_per_step"]

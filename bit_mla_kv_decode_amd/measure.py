@@ -15,10 +15,11 @@
                  8 x 131072 C4R4 cache: 16 heads x s_q 1..8, 128 heads x 2
       - proj:    the absorbed projections (mla_absorb_q, mla_project_out) at
                  128 heads, batch 8..128: weight GB/s
-  python -m bit_mla_kv_decode_amd.measure --counters [--heads H]
+  python -m bit_mla_kv_decode_amd.measure --counters [--workload W] [--format F] [--heads H]
       the launches a rocprofv3 --pmc run counts: a 1 GiB plain copy three
-      times, then the 8 x 131072 C4R4 decode (bench configuration: fused append +
-      balanced partial; with --heads, the first H of its 128 heads) three times
+      times, then the decode of workload W (default the 8 x 131072 C4R4 cache;
+      its data in format F if given) in the bench configuration (fused append +
+      balanced partial; with --heads, the first H of its heads) three times
   python -m bit_mla_kv_decode_amd.measure --parse-counters FETCH.csv WRITE.csv
       per-launch HBM bytes of the decode kernel from FETCH_SIZE / WRITE_SIZE,
       each scaled by what the counter reads for the copy of known size
@@ -308,9 +309,11 @@ SECTIONS = {"peaks": section_peaks, "configs": section_configs, "bf16": section_
 
 # ------------------------------------------------------------------ counters
 
-def run_counters(heads=0):
-    """The launches one rocprofv3 --pmc pass counts (kernel names tell them apart);
-    heads > 0 decodes with the first `heads` heads of the workload's queries."""
+def run_counters(heads=0, workload="c4r4_128k", fmt=""):
+    """The launches one rocprofv3 --pmc pass counts (kernel names tell them apart):
+    a plain copy, then the bench step's decode launch on `workload` (its cache
+    in format `fmt` if given); heads > 0 decodes with the first `heads` heads
+    of the workload's queries."""
     import torch
     import bit_mla_kv_decode_amd as mla
     from bit_mla_kv_decode_amd import peaks
@@ -324,7 +327,8 @@ def run_counters(heads=0):
     torch.cuda.synchronize()
     del src, dst
     log("copy: 3 x %d bytes" % n)
-    c = Case(W.WORKLOADS["c4r4_128k"])
+    w0 = W.WORKLOADS[workload]
+    c = Case(W.derive(w0, fmt=fmt) if fmt else w0)
     w, B = c.w, c.w.batch
     H = heads if heads > 0 else w.heads
     q = c.q[:, :H].contiguous()
@@ -333,7 +337,8 @@ def run_counters(heads=0):
         mla.mla_decode_append_partial(w.fmt, c.new_lat, c.new_rope, q, c.caches[i % len(c.caches)], c.btd, c.sld,
                                       w.softmax_scale, 0, ws, max_seq_len=int(c.lens.max()), stream=st)
     torch.cuda.synchronize()
-    log("decode: 3 launches, %d heads, %d packed bytes each, %d replicas" % (H, c.packed, len(c.caches)))
+    log("decode: 3 launches, %s %s, %d heads, %d packed bytes each, %d replicas"
+        % (w.name, w.fmt, H, c.packed, len(c.caches)))
     print(json.dumps({"copy_bytes": n, "packed_bytes": c.packed}), flush=True)
 
 
@@ -413,6 +418,8 @@ def main():
     ap.add_argument("--only", default=",".join(SECTIONS))
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--heads", type=int, default=0, help="with --counters: decode this many heads (default all 128)")
+    ap.add_argument("--workload", default="c4r4_128k", help="with --counters: the workload whose decode is counted")
+    ap.add_argument("--format", default="", help="with --counters: its cache in this format instead (same data)")
     ap.add_argument("--parse-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--packed-bytes", type=int, default=None)
     ap.add_argument("--parse-pmc", nargs="+", metavar="CSV")
@@ -429,7 +436,7 @@ def main():
         raise SystemExit("measure needs a GPU")
     mla.load_library()
     if args.counters:
-        run_counters(args.heads)
+        run_counters(args.heads, args.workload, args.format)
         return
     for s in args.only.split(","):
         SECTIONS[s]()

@@ -64,3 +64,11 @@ def test_kernel_hash_ignores_comments_not_code(tmp_path, monkeypatch):
         monkeypatch.setattr(bench, "ROOT", tree(code))
         hashes.append(bench.kernel_source_sha256())
     assert hashes[0] == hashes[1] != hashes[2]
+
+
+def test_traffic_tags_name_workload_format_and_heads():
+    import bench
+    assert bench.traffic_tag("c4r4_128k") == "c4r4_128k"
+    assert bench.traffic_tag("c2r4_32k_outliers", "BF16") == "c2r4_32k_outliers_bf16"
+    assert bench.traffic_tag("c4r4_128k", "", 16) == "c4r4_128k_h16"
+
