@@ -188,18 +188,21 @@ def time_case(w, args, fused, S, dev, label=None, tag=None):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
-    def step(i, timed=None):
-        c = caches[i % replicas]
-        if not fused:
-            mla.mla_quant_append(w.fmt, new_lat, new_rope, new_slots, c, stream=stream)
-        if timed is not None:
-            timed[0].record(stream)
+    def decode(c):
         if fused:
             mla.mla_decode_append_partial(w.fmt, new_lat, new_rope, q, c, bt_d, sl_d, w.softmax_scale, S, ws,
                                           max_seq_len=max_len, stream=stream)
         else:
             mla.mla_decode_partial(w.fmt, q, c, bt_d, sl_d, w.softmax_scale, S, ws, max_seq_len=max_len,
                                    stream=stream)
+
+    def step(i, timed=None):
+        c = caches[i % replicas]
+        if not fused:
+            mla.mla_quant_append(w.fmt, new_lat, new_rope, new_slots, c, stream=stream)
+        if timed is not None:
+            timed[0].record(stream)
+        decode(c)
         if timed is not None:
             timed[1].record(stream)
         mla.mla_decode_combine(w.fmt, B, H, S, ws, out, lse, stream=stream)
@@ -213,7 +216,17 @@ def time_case(w, args, fused, S, dev, label=None, tag=None):
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
     ms_step = total * 1e3 / args.steps
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    k_ms_step = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the decode kernel's average launch duration: the same launches back to
+    # back between two events on its stream, so that the events' own dispatch
+    # gap (several us per pair) is paid once, not per launch
+    burst = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    burst[0].record(stream)
+    for i in range(args.steps):
+        decode(caches[i % replicas])
+    burst[1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = burst[0].elapsed_time(burst[1]) / args.steps
     value = packed_bytes / (ms_step * 1e-3) / 1e9
     k_gbs = packed_bytes / (k_ms * 1e-3) / 1e9
     k_tflops = flops / (k_ms * 1e-3) / 1e12
@@ -232,7 +245,8 @@ def time_case(w, args, fused, S, dev, label=None, tag=None):
                 "bound": bound, "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": counted_traffic(tag) if (tag and S == 0 and fused) else None,
-                "kernel_ms": round(k_ms, 4), "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
+                "kernel_ms": round(k_ms, 4), "kernel_ms_events_per_step": round(k_ms_step, 4),
+                "flops_per_launch": flops, "packed_bytes_per_launch": packed_bytes,
                 "intensity_flop_per_byte": round(intensity, 1),
                 "kernel_packed_gbs": round(k_gbs, 2), "kernel_hbm_peak_frac": round(k_gbs / HBM_PEAK_GBS, 4)}
     res = {"workload": w.name, "format": w.fmt, "batch": B, "heads": H, "ctx": max_len, "tokens": tokens,

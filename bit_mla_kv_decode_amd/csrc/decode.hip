@@ -1054,10 +1054,15 @@ struct IwAcc {
 
 // Row r of a wavefront's V buffer (token r of the tile) starts at element
 // vrow(r): rows 528 bf16 (1056 bytes) apart, rows 8..15 and 24..31 shifted by
-// 16 bytes, so that the rows a 16-byte write touches (16 tokens of a block)
-// and the rows a transposing read touches (8 tokens per 32 lanes) fall on
-// distinct LDS banks.
+// 16 bytes.  In rows whose bit 2 is set (vswap) the two 16-byte halves of
+// every 32-byte channel pair trade places.  The LDS serves 16-byte writes
+// eight lanes at a time over 32 four-byte banks and reads 256 bytes at a time
+// over 64 banks (the bank-conflict counter of this kernel and of the >16-row
+// kernels shows both); with this layout the 8 rows of an 8-lane write group
+// and the 8 rows x 32 bytes of a 32-lane transposing read each cover
+// distinct banks, which no layout with one shift per row achieves.
 __device__ __forceinline__ constexpr int vrow(int r) { return r * kVRow + 8 * ((r >> 3) & 1); }
+__device__ __forceinline__ constexpr int vswap(int r) { return (r >> 2) & 1; }
 
 // Q.K^T k-step order: the RoPE k-steps first (they write no V), then the
 // content blocks in channel order.
@@ -1097,15 +1102,19 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   // reads tokens 4 kg + j of block 0 (then of block 1), lane 4 j + r of the
   // block channels 4 r .. + 4 of the channel tile; lane i of the block
   // receives channel i of those 4 tokens
-  const __bf16* __restrict__ vtr = vbuf + vrow(4 * g + ((lane & 15) >> 2)) + 4 * (lane & 3);
+  const int trow = 4 * g + ((lane & 15) >> 2);
+  const __bf16* __restrict__ vtr = vbuf + vrow(trow) + 8 * (((lane & 3) >> 1) ^ vswap(trow)) + 4 * (lane & 1);
   auto tr_read = [&](int ct) {
     const __bf16* v0 = vtr + 16 * ct;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v0);
     const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + vrow(16)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  __bf16* __restrict__ vw0 = vbuf + vrow(t);
-  __bf16* __restrict__ vw1 = vbuf + vrow(16 + t);
+  // the lane's rows t and 16 + t; even / odd 16-byte chunks of its channels
+  // land one chunk up / down in swapped rows
+  __bf16* __restrict__ vw0e = vbuf + vrow(t) + 8 * vswap(t);
+  __bf16* __restrict__ vw0o = vbuf + vrow(t) - 8 * vswap(t);
+  constexpr int kVw1 = vrow(16) - vrow(0);   // vrow(16 + t) - vrow(t), vswap alike
   const SubLanes lo = SF::lanes(t, g);
 
   SF f0, f1;  // blocks 0 and 1 of the tile
@@ -1153,8 +1162,9 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
     const bf16x8 qk = qv[p & 3];
     if (p + 4 < 18) qv[p & 3] = *(const bf16x8*)(qlds + iw_chan(iw_ks(p + 4), g));
     if (ks < 16) {
-      *(bf16x8*)(vw0 + iw_chan(ks, g)) = k0;
-      *(bf16x8*)(vw1 + iw_chan(ks, g)) = k1;
+      __bf16* vw = (ks & 1) ? vw0o : vw0e;  // chunk iw_chan / 8 has the parity of ks
+      *(bf16x8*)(vw + iw_chan(ks, g)) = k0;
+      *(bf16x8*)(vw + kVw1 + iw_chan(ks, g)) = k1;
     }
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qk, s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qk, s1, 0, 0, 0);
