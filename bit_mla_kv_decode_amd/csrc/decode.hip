@@ -902,9 +902,9 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t 
 //      in its lane (channels iw_chan(ks, g) .. + 8) are one code dword;
 //   2. dequantizes k-step by k-step in registers, straight into the A operand
 //      of MFMA 16x16x32 bf16 (16 tokens x 32 channels), one MFMA per block
-//      sharing B = q^T read from LDS (the rows of the piece are staged once
-//      per piece); the content values also go to the wavefront's own LDS
-//      buffer for step 4.  Output: S^T, lane (h, g) holding row h for tokens
+//      sharing B = q^T (the rows of the piece are staged in LDS once per
+//      piece and held in registers for the pass); the content values also go
+//      to the wavefront's own LDS buffer for step 4.  Output: S^T, lane (h, g) holding row h for tokens
 //      4 g .. 4 g + 3 of each block;
 //   3. takes the eight softmax weights of its lane against a fixed reference
 //      per wavefront and pass (as in split_pass) and splits them into high
@@ -974,30 +974,42 @@ __device__ __forceinline__ constexpr int iw_chan(int ks, int g) {
   return ks < 16 ? 128 * (ks >> 2) + 32 * g + 8 * (ks & 3) : kDc + 32 * (ks - 16) + 8 * g;
 }
 
+// Per-lane byte offsets within a page: content codes, content S/Z, RoPE codes,
+// RoPE S/Z.  The loads are buffer loads: the page is a buffer resource in
+// scalar registers (built once per tile), the uniform part of each offset a
+// scalar or immediate, and only this 32-bit offset lives per lane, so no load
+// needs 64-bit address arithmetic in the vector ALU (and none can leave the
+// page: bytes past the resource's size read as zero).
 struct SubLanes {
-  int c, sz, rc, rsz;  // per-lane byte offsets: content codes, content S/Z, RoPE codes, RoPE S/Z
+  unsigned c, sz, rc, rsz;
 };
+// word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, no stride
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* page_base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page_base), 0, bytes, kBufWord3);
+}
 
 template <int F> struct SubFill;
 
 template <> struct SubFill<kC4R4> {
   using Lay = PageLayout<kC4R4>;
   // block m of lane group g: chunk 4 m + g (16 bytes: 32 channels), group 2 m + g / 2
-  static __device__ __forceinline__ SubLanes lanes(int t, int g) {
+  static __device__ __forceinline__ SubLanes lanes(unsigned t, unsigned g) {
     return SubLanes{16 * t + 1024 * g, 4 * t + 256 * (g >> 1), 16 * t + 4 * g, 4 * t};
   }
   u32x4 c[4];
   unsigned sz[4];
   unsigned r[2];    // dword g of RoPE chunks 0, 1
   unsigned rsz;
-  __device__ __forceinline__ void issue(int i, const uint8_t* pb, int hp, const SubLanes& o) {
+  __device__ __forceinline__ void issue(int i, __amdgpu_buffer_rsrc_t pg, int hp, const SubLanes& o) {
     if (i < 4) {
-      c[i] = *(const u32x4*)(pb + Lay::kCodesA + 256 * hp + 4096 * i + o.c);
-      sz[i] = *(const unsigned*)(pb + Lay::kSzB + 64 * hp + 512 * i + o.sz);
+      c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pg, o.c, Lay::kCodesA + 256 * hp + 4096 * i, 0));
+      sz[i] = __builtin_amdgcn_raw_buffer_load_b32(pg, o.sz, Lay::kSzB + 64 * hp + 512 * i, 0);
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) r[j] = *(const unsigned*)(pb + Lay::kCodesC + 256 * hp + 1024 * j + o.rc);
-      rsz = *(const unsigned*)(pb + Lay::kSzD + 64 * hp + o.rsz);
+      for (int j = 0; j < 2; ++j)
+        r[j] = __builtin_amdgcn_raw_buffer_load_b32(pg, o.rc, Lay::kCodesC + 256 * hp + 1024 * j, 0);
+      rsz = __builtin_amdgcn_raw_buffer_load_b32(pg, o.rsz, Lay::kSzD + 64 * hp, 0);
     }
   }
   __device__ __forceinline__ unsigned sz_of(int ks, bool live) const {
@@ -1012,7 +1024,7 @@ template <> struct SubFill<kC2R4> {
   using Lay = PageLayout<kC2R4>;
   // block m of lane group g: bytes 8 (g & 1) .. + 8 of chunk 2 m + g / 2 (32
   // channels), group 4 m + g
-  static __device__ __forceinline__ SubLanes lanes(int t, int g) {
+  static __device__ __forceinline__ SubLanes lanes(unsigned t, unsigned g) {
     return SubLanes{16 * t + 1024 * (g >> 1) + 8 * (g & 1), 4 * t + 256 * g, 16 * t + 4 * g, 4 * t};
   }
   u32x2 c[4];
@@ -1020,14 +1032,15 @@ template <> struct SubFill<kC2R4> {
   unsigned r[2];
   unsigned rsz;
   unsigned b[4];    // masked code bytes of the dword being converted
-  __device__ __forceinline__ void issue(int i, const uint8_t* pb, int hp, const SubLanes& o) {
+  __device__ __forceinline__ void issue(int i, __amdgpu_buffer_rsrc_t pg, int hp, const SubLanes& o) {
     if (i < 4) {
-      c[i] = *(const u32x2*)(pb + Lay::kCodesA + 256 * hp + 2048 * i + o.c);
-      sz[i] = *(const unsigned*)(pb + Lay::kSzB + 64 * hp + 1024 * i + o.sz);
+      c[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(pg, o.c, Lay::kCodesA + 256 * hp + 2048 * i, 0));
+      sz[i] = __builtin_amdgcn_raw_buffer_load_b32(pg, o.sz, Lay::kSzB + 64 * hp + 1024 * i, 0);
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) r[j] = *(const unsigned*)(pb + Lay::kCodesC + 256 * hp + 1024 * j + o.rc);
-      rsz = *(const unsigned*)(pb + Lay::kSzD + 64 * hp + o.rsz);
+      for (int j = 0; j < 2; ++j)
+        r[j] = __builtin_amdgcn_raw_buffer_load_b32(pg, o.rc, Lay::kCodesC + 256 * hp + 1024 * j, 0);
+      rsz = __builtin_amdgcn_raw_buffer_load_b32(pg, o.rsz, Lay::kSzD + 64 * hp, 0);
     }
   }
   __device__ __forceinline__ unsigned sz_of(int ks, bool live) const {
@@ -1084,7 +1097,9 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
                                         int limit, bool fixed, float m_fixed, IwAcc& acc) {
   using SF = SubFill<F>;
   const int limit_min = L - (a.s_q - 1);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wavefront index as a scalar: tile indices, page offsets and load
+  // offsets derived from it stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int t = lane & 15, g = lane >> 4;  // QK operand lane: token t, channel quarter g; S^T lane: row t, tokens 4 g..
   __bf16* __restrict__ vbuf = smem + wave * kVBuf;
   const __bf16* __restrict__ qlds = smem + kIwWaves * kVBuf + t * kIwQRow;
@@ -1118,17 +1133,19 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   const SubLanes lo = SF::lanes(t, g);
 
   SF f0, f1;  // blocks 0 and 1 of the tile
-  const uint8_t* pb = nullptr;
+  __amdgpu_buffer_rsrc_t pg = page_rsrc(a.cache, PageLayout<F>::kBytes);
   int hpt = 0;   // half of the page of the tile whose bytes issue() loads next
   int pg_next = win.page_of(ufirst);
   auto aim = [&](int page, int u) {
+    page = __builtin_amdgcn_readfirstlane(page);  // uniform: keeps the resource in scalar registers
     const bool ok = page >= 0 && page < a.num_pages;
-    pb = a.cache + (ok ? page : 0) * (int64_t)PageLayout<F>::kBytes;  // an invalid page reads page 0, zeroed
+    // an invalid page reads page 0, zeroed
+    pg = page_rsrc(a.cache + (ok ? page : 0) * (int64_t)PageLayout<F>::kBytes, PageLayout<F>::kBytes);
     hpt = u & 1;
   };
   auto issue = [&](int i) {
-    f0.issue(i, pb, 2 * hpt, lo);
-    f1.issue(i, pb, 2 * hpt + 1, lo);
+    f0.issue(i, pg, 2 * hpt, lo);
+    f1.issue(i, pg, 2 * hpt + 1, lo);
   };
   aim(pg_next, ufirst);
 #pragma unroll
@@ -1136,7 +1153,11 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
 
   // ---- Q.K^T state of the tile being dequantized
   f32x4 s0, s1;
-  bf16x8 qv[4];
+  // the q operand of every k-step stays in registers for the pass (72 of
+  // them: one wavefront per SIMD leaves room), read from LDS once
+  bf16x8 qall[18];
+#pragma unroll
+  for (int d = 0; d < 18; ++d) qall[d] = *(const bf16x8*)(qlds + iw_chan(iw_ks(d), g));
   float S0 = 0.0f, Z0 = 0.0f, S1 = 0.0f, Z1 = 0.0f;
   bool live0 = false, live1 = false;
   auto qk_begin = [&](int u) {
@@ -1148,8 +1169,6 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
     aim(pg_next, un);
     s0 = (f32x4){};
     s1 = (f32x4){};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) qv[d] = *(const bf16x8*)(qlds + iw_chan(iw_ks(d), g));
   };
   auto qk_step = [&](int p) {
     const int ks = iw_ks(p);
@@ -1159,8 +1178,7 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
     }
     const bf16x8 k0 = f0.step(ks, S0, Z0);
     const bf16x8 k1 = f1.step(ks, S1, Z1);
-    const bf16x8 qk = qv[p & 3];
-    if (p + 4 < 18) qv[p & 3] = *(const bf16x8*)(qlds + iw_chan(iw_ks(p + 4), g));
+    const bf16x8 qk = qall[p];
     if (ks < 16) {
       __bf16* vw = (ks & 1) ? vw0o : vw0e;  // chunk iw_chan / 8 has the parity of ks
       *(bf16x8*)(vw + iw_chan(ks, g)) = k0;
