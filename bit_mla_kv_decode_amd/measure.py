@@ -74,7 +74,7 @@ def _events(fn, iters, warmup, stream):
 class Case:
     """A workload's caches (replicated past the 256 MB last-level cache) and decode buffers."""
 
-    def __init__(self, w, min_total=1.0e9):
+    def __init__(self, w, min_total=1.0e9, rows_hook=None):
         import torch
         import bit_mla_kv_decode_amd as mla
         from bit_mla_kv_decode_amd import workloads as W
@@ -88,6 +88,8 @@ class Case:
             for t0 in range(0, end, 32768):
                 t1 = min(end, t0 + 32768)
                 lat, rope = W.sequence_rows(w, b, t0, t1, "cuda")
+                if rows_hook is not None:
+                    rows_hook(b, t0, t1, lat)
                 mla.mla_quant_append(w.fmt, lat, rope, torch.from_numpy(W.slots_for(self.bt, b, t0, t1)).cuda(), first)
         self.new_lat, self.new_rope = W.new_token_rows(w, self.lens, "cuda")
         self.new_slots = torch.from_numpy(np.array([W.slots_for(self.bt, b, int(L) - 1, int(L))[0]
@@ -303,8 +305,44 @@ def section_proj():
         torch.cuda.empty_cache()
 
 
+def section_recompute():
+    """Cost of the fixed-reference recompute: the 8 x 131072 C4R4 cache with
+    keys far above the rest a few tiles into every 4096-token balanced share
+    (channel 0 = 60 .. 63 at share offsets 300, 332, 364, 396, so every
+    wavefront of the <= 16-row kernel meets one after its first tile).  With
+    q[:, :, 0] = 0 those keys are harmless; with q[:, :, 0] in [30, 40) their
+    logits rise more than kRefLift + kMaxLift = 120 log2 units above each
+    piece's first tile, so every piece is computed twice.  `share` selects
+    every share (worst case) or one share in 32 (one per sequence)."""
+    import torch
+    from bit_mla_kv_decode_amd import workloads as W
+    for every in (1, 32):
+        def hook(b, t0, t1, lat, every=every):
+            for s0 in range(0, int(W.seq_lens(W.WORKLOADS["c4r4_128k"])[b]), 4096 * every):
+                for j in range(4):
+                    t = s0 + 300 + 32 * j
+                    if t0 <= t < t1:
+                        lat[t - t0, 0] = 60.0 + j
+        case = Case(W.WORKLOADS["c4r4_128k"], rows_hook=hook)
+        g = torch.Generator(device="cuda").manual_seed(7)
+        for H in (128, 16):
+            q = case.q[:, :H].contiguous()
+            q_off = q.clone()
+            q_off[:, :, 0] = 0
+            q_on = q.clone()
+            q_on[:, :, 0] = (30.0 + 10.0 * torch.rand(q.shape[0], H, device="cuda", generator=g)).to(q.dtype)
+            t_off = case.time(0, iters=20, warmup=50, q=q_off)[0]
+            t_on = case.time(0, iters=20, warmup=50, q=q_on)[0]
+            emit({"row": "recompute", "heads": H, "shares_with_jump": "all" if every == 1 else "1 of 32",
+                  "decode_ms_no_jump": round(t_off, 4), "decode_ms_jump": round(t_on, 4),
+                  "slowdown": round(t_on / t_off, 3)})
+        del case
+        torch.cuda.empty_cache()
+
+
 SECTIONS = {"peaks": section_peaks, "configs": section_configs, "bf16": section_bf16,
-            "heads": section_heads, "pages": section_pages, "multi": section_multi, "proj": section_proj}
+            "heads": section_heads, "pages": section_pages, "multi": section_multi, "proj": section_proj,
+            "recompute": section_recompute}
 
 
 # ------------------------------------------------------------------ counters
