@@ -340,9 +340,75 @@ def section_recompute():
         torch.cuda.empty_cache()
 
 
+def _smi_sample():
+    """Socket power (W) and the GFX clocks (MHz) amd-smi reports, or None."""
+    import re
+    import subprocess
+    try:
+        t = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    p = re.findall(r"SOCKET_POWER: (\d+) W", t)
+    c = [int(x) for x in re.findall(r"^\s+CLK: (\d+) MHz", t, re.M)][:8]
+    return {"socket_power_W": int(p[0]) if p else None, "gfx_clk_MHz": c}
+
+
+def section_power(seconds=14.0):
+    """Socket power and GFX clocks while one kind of launch runs back to back:
+    the decode of three workloads (and the BF16 cache) and the dense MFMA loop
+    of the peaks section.  Samples are taken after 8 and 11 seconds, once the
+    power controller has settled; the board's cap is 1400 W."""
+    import threading
+    import time
+    import torch
+    import bit_mla_kv_decode_amd as mla
+    from bit_mla_kv_decode_amd import peaks
+    from bit_mla_kv_decode_amd import workloads as W
+    st = torch.cuda.current_stream()
+    emit({"row": "power_idle", **(_smi_sample() or {})})
+    runs = [("c4r4_128k", 128, ""), ("c4r4_128k", 16, ""), ("c2r4_32k_outliers", 128, ""),
+            ("c2r4_32k_outliers", 128, "BF16"), ("mfma", 0, "")]
+    for name, H, fmt in runs:
+        if name == "mfma":
+            sink = torch.zeros(2048 * 256, dtype=torch.float32, device="cuda")
+            fl = peaks.mfma_bf16(2048, 4000, sink, st)
+            launch = lambda i: peaks.mfma_bf16(2048, 4000, sink, st)
+            per, unit = fl / 1e12, "TFLOP"
+        else:
+            w = W.WORKLOADS[name]
+            if fmt:
+                w = W.derive(w, fmt=fmt)
+            c = Case(w)
+            q = c.q[:, :H].contiguous()
+            ws = torch.empty(mla.mla_decode_workspace_bytes(w.fmt, w.batch, H, 0), dtype=torch.uint8, device="cuda")
+            mx = int(c.lens.max())
+            launch = lambda i, c=c, q=q, ws=ws, w=w, mx=mx: mla.mla_decode_partial(
+                w.fmt, q, c.caches[i % len(c.caches)], c.btd, c.sld, w.softmax_scale, 0, ws, max_seq_len=mx, stream=st)
+            per, unit = c.packed / 1e9, "GB"
+        samples = []
+        timer = [threading.Timer(d, lambda: samples.append(_smi_sample())) for d in (8.0, 11.0)]
+        t0 = time.time()
+        for tm in timer:
+            tm.start()
+        n = 0
+        while time.time() - t0 < seconds:
+            for i in range(10):
+                launch(i)
+            torch.cuda.synchronize()
+            n += 10
+        dt = time.time() - t0
+        for tm in timer:
+            tm.join()
+        emit({"row": "power", "run": name if name == "mfma" else "%s %s %d heads" % (name, fmt or W.WORKLOADS[name].fmt, H),
+              "us_per_launch": round(dt / n * 1e6, 1), "rate": round(per * n / dt, 1), "rate_unit": unit + "/s",
+              "samples": samples})
+        launch = None
+        torch.cuda.empty_cache()
+
+
 SECTIONS = {"peaks": section_peaks, "configs": section_configs, "bf16": section_bf16,
             "heads": section_heads, "pages": section_pages, "multi": section_multi, "proj": section_proj,
-            "recompute": section_recompute}
+            "recompute": section_recompute, "power": section_power}
 
 
 # ------------------------------------------------------------------ counters
