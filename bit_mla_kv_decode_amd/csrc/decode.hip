@@ -1883,8 +1883,8 @@ static hipError_t set_lds(K kernel, size_t bytes, std::atomic<unsigned long long
 // 17..32 rows (two workgroups per compute unit),
 // 2 wavefronts per group for 33..64 rows, else one head group per wavefront
 // (the unquantized baseline always uses the latter).  On 8 x 131072 C4R4
-// tokens, balanced: 16 heads 0.222 -> 0.167 ms (channel split) -> 0.146 ms
-// (independent wavefronts), 64 heads 0.309 -> 0.283 ms.
+// tokens, balanced: 16 heads 0.222 -> 0.167 ms (channel split) -> 0.11 ms
+// (independent wavefronts), 64 heads 0.309 -> 0.27 ms.
 static int channel_split(int fmt, int rows) {
   if (fmt == kBF16) return 1;
   return rows <= 16 ? 0 : rows <= 32 ? 4 : rows <= 64 ? 2 : 1;

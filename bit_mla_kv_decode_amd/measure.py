@@ -1,13 +1,14 @@
 """Measurements of the low-bit MLA decode path on one GPU.
 
-  python -m bit_mla_kv_decode_amd.measure [--only peaks,configs,bf16,heads,pages]
+  python -m bit_mla_kv_decode_amd.measure [--only peaks,configs,bf16,heads,pages,...]
       JSON lines on stdout, one per measured row (progress on stderr):
       - peaks:   practical peaks from the microbenchmarks (streaming HBM read,
                  plain copy, dense bf16 MFMA loop)
       - configs: every workload: decode partial / combine / append times
-                 (median of per-launch HIP events), packed GB/s, TFLOP/s and
-                 the roofline fraction max(t_HBM, t_MFMA) / t; balanced and
-                 fixed-split partitions
+                 (median over bursts of back-to-back launches, each burst
+                 timed by HIP events, after a warm-up), packed GB/s, TFLOP/s
+                 and the roofline fraction max(t_HBM, t_MFMA) / t; balanced
+                 and fixed-split partitions
       - bf16:    the unquantized-cache kernel on the C2R4 workload's data
       - heads:   head-count sweep at the 8 x 131072 C4R4 shape
       - pages:   contiguous vs randomly permuted page tables
@@ -15,6 +16,9 @@
                  8 x 131072 C4R4 cache: 16 heads x s_q 1..8, 128 heads x 2
       - proj:    the absorbed projections (mla_absorb_q, mla_project_out) at
                  128 heads, batch 8..128: weight GB/s
+      - recompute: full-size cost of the fixed-reference softmax's second pass
+      - power:   socket power and GFX clocks (amd-smi) under back-to-back
+                 decode launches and the dense MFMA loop
   python -m bit_mla_kv_decode_amd.measure --counters [--workload W] [--format F] [--heads H]
       the launches a rocprofv3 --pmc run counts: a 1 GiB plain copy three
       times, then the decode of workload W (default the 8 x 131072 C4R4 cache;
@@ -57,22 +61,32 @@ def flops_per_token(heads):
 
 # ------------------------------------------------------------------ timing helpers
 
-def _events(fn, iters, warmup, stream):
+def _events(fn, iters, warmup, stream, burst=10):
+    """Per-launch times (ms) of fn: after at least `warmup` calls and 60 ms of
+    back-to-back launches (the clocks settle within ~50 ms), `iters` bursts of
+    `burst` launches, each timed by a pair of HIP events on `stream`."""
+    import time
     import torch
-    for _ in range(warmup):
-        fn(0)
+    t0, n = time.perf_counter(), 0
+    while n < warmup or time.perf_counter() - t0 < 0.06:
+        fn(n)
+        n += 1
+        if n % 20 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i, (a, b) in enumerate(ev):
         a.record(stream)
-        fn(i + 1)
+        for j in range(burst):
+            fn(i * burst + j + 1)
         b.record(stream)
     torch.cuda.synchronize()
-    return np.array([a.elapsed_time(b) for a, b in ev])
+    return np.array([a.elapsed_time(b) / burst for a, b in ev])
 
 
 class Case:
-    """A workload's caches (replicated past the 256 MB last-level cache) and decode buffers."""
+    """A workload's caches (replicated past the 256 MB last-level cache) and decode buffers.
+    Timings are per-launch averages of back-to-back bursts after a warm-up (see _events)."""
 
     def __init__(self, w, min_total=1.0e9, rows_hook=None):
         import torch
