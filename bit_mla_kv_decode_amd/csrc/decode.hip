@@ -42,6 +42,7 @@
 //      with one split, the final bf16 output directly).
 // A second kernel merges the pieces with log-sum-exp weights.
 #include <atomic>
+#include <type_traits>
 
 #include "append.h"
 #include "kernels.h"
@@ -1139,8 +1140,9 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   auto aim = [&](int page, int u) {
     page = __builtin_amdgcn_readfirstlane(page);  // uniform: keeps the resource in scalar registers
     const bool ok = page >= 0 && page < a.num_pages;
-    // an invalid page reads page 0, zeroed
-    pg = page_rsrc(a.cache + (ok ? page : 0) * (int64_t)PageLayout<F>::kBytes, PageLayout<F>::kBytes);
+    // an invalid page id gets an empty resource: its loads read zeros (codes
+    // 0, S = Z = 0), so its rows dequantize to exact zeros
+    pg = page_rsrc(a.cache + (ok ? page : 0) * (int64_t)PageLayout<F>::kBytes, ok ? PageLayout<F>::kBytes : 0);
     hpt = u & 1;
   };
   auto issue = [&](int i) {
@@ -1170,11 +1172,14 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
     s0 = (f32x4){};
     s1 = (f32x4){};
   };
-  auto qk_step = [&](int p) {
+  // rows past the sequence end are zeroed through S = Z = 0; only tiles that
+  // may hold such rows (kMask) pay for the selects
+  auto qk_step = [&](int p, auto kMask) {
+    constexpr bool kM = decltype(kMask)::value;
     const int ks = iw_ks(p);
     if (ks % 4 == 0 || ks == 16) {
-      sz_unpack(f0.sz_of(ks, live0), S0, Z0);
-      sz_unpack(f1.sz_of(ks, live1), S1, Z1);
+      sz_unpack(f0.sz_of(ks, !kM || live0), S0, Z0);
+      sz_unpack(f1.sz_of(ks, !kM || live1), S1, Z1);
     }
     const bf16x8 k0 = f0.step(ks, S0, Z0);
     const bf16x8 k1 = f1.step(ks, S1, Z1);
@@ -1192,9 +1197,12 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   // ---- softmax of a finished Q.K^T: weights against the reference, high /
   //      low bf16 halves, already in the lane's slots of the P.V operand
   bf16x8 bph, bpl;
-  auto softmax = [&](int u) {
+  // kMask: the tile may hold tokens past a row's limit (or the sequence
+  // end); the loop below runs the tiles that cannot with kMask = false, so
+  // the compares and selects are not executed on every tile
+  auto softmax = [&](int u, auto kMask) {
     f32x4 s[2] = {s0, s1};
-    if (kIwTok * (u + 1) > limit_min) {  // the tokens past the row's limit (and the sequence end)
+    if (decltype(kMask)::value && kIwTok * (u + 1) > limit_min) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int lt = limit - kIwTok * u - 16 * b - 4 * g;
@@ -1250,21 +1258,25 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   // prologue: Q.K^T and weights of the first tile
   qk_begin(ufirst);
 #pragma unroll
-  for (int p = 0; p < 18; ++p) qk_step(p);
-  softmax(ufirst);
-  int u = ufirst;
-  for (; u + kIwWaves < u1; u += kIwWaves) {
-    // P.V of tile u interleaved with Q.K^T of tile u + 4
+  for (int p = 0; p < 18; ++p) qk_step(p, std::true_type{});
+  softmax(ufirst, std::true_type{});
+  // P.V of tile u interleaved with Q.K^T of tile u + 4
+  auto step_tile = [&](int u, auto kMask) {
     qk_begin(u + kIwWaves);
     pv_start();
 #pragma unroll
     for (int p = 0; p < 18; ++p) {
-      qk_step(p);
+      qk_step(p, kMask);
 #pragma unroll
       for (int ct = pv_begin(p); ct < pv_end(p); ++ct) pv_tile(ct);
     }
-    softmax(u + kIwWaves);
-  }
+    softmax(u + kIwWaves, kMask);
+  };
+  // tiles from u_mask on may hold tokens past a row's limit
+  const int u_mask = limit_min >> 5;
+  int u = ufirst;
+  for (; u + kIwWaves < u1 && u + kIwWaves < u_mask; u += kIwWaves) step_tile(u, std::false_type{});
+  for (; u + kIwWaves < u1; u += kIwWaves) step_tile(u, std::true_type{});
   // epilogue: P.V of the last tile
   pv_start();
 #pragma unroll
