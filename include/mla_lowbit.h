@@ -155,7 +155,10 @@ int64_t mla_decode_partial_slots(const mla_format_t* fmt, int32_t batch, int32_t
  *   q_bf16        [batch, num_heads, d_c + d_r]  absorbed content query then
  *                                                RoPE query, per head
  *   cache         as written by mla_quant_append, num_pages pages
- *   block_table   [batch, max_pages_per_seq] int32 physical page ids
+ *   block_table   [batch, max_pages_per_seq] int32 physical page ids; an
+ *                 id outside [0, num_pages) within a sequence's length reads
+ *                 as a page of zero rows (logit 0, value 0), never out of
+ *                 the pool
  *   seq_lens      [batch] int32 tokens per sequence (0 gives out = 0 and
  *                 lse = -inf; values above max_pages_per_seq * page_size are
  *                 clamped to that capacity)

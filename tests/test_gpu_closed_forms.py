@@ -188,3 +188,42 @@ def test_piece_longer_than_page_window(fmt, heads):
             splits, int(bad.sum()), bad.size, float(err.max()))
         l = lse.cpu().numpy()
         assert np.allclose(l, ref_lse, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("fmt", ["C4R4", "C2R4", "BF16"])
+@pytest.mark.parametrize("heads", [8, 24, 48, 128])
+def test_invalid_page_ids_read_as_zero_rows(fmt, heads):
+    """Block-table entries outside [0, num_pages) inside a sequence's length
+    read as rows of zeros (logit 0, value 0) in every kernel variant: the
+    same result as pointing them at an all-zero page, which the oracle
+    dequantizes to exact zeros."""
+    import bit_mla_kv_decode_amd.workloads as W
+    _say("invalid pages %s H=%d" % (fmt, heads))
+    lens = np.array([700, 300, 2100], np.int32)
+    w = W.Workload("badpages", fmt, batch=len(lens), heads=heads, outliers=fmt == "C2R4", pages="random",
+                   seed=heads + 70)
+    bt, npages = W.page_table(w, lens, 2)
+    cache = mla.alloc_cache(fmt, npages + 1)   # page npages stays zero
+    for b, L in enumerate(lens):
+        la, ro = W.sequence_rows(w, b, 0, int(L), "cuda")
+        mla.mla_quant_append(fmt, la, ro, torch.from_numpy(W.slots_for(bt, b, 0, int(L))).cuda(), cache)
+    bad = bt.copy()
+    bad[0, 3] = -1
+    bad[2, 1] = npages + 7
+    bad[2, 20] = -5
+    zero_bt = bad.copy()
+    zero_bt[(bad < 0) | (bad >= npages + 1)] = npages
+    q = W.queries(w, "cpu")
+    host = cache.cpu().numpy()
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, host, npages + 1, zero_bt, lens, SCALE)
+    for splits in (0, 1, 3):
+        lse = torch.empty(len(lens), heads, dtype=torch.float32, device="cuda")
+        out, _ = mla.mla_decode_lowbit(fmt, q.cuda(), cache, torch.from_numpy(bad).cuda(),
+                                       torch.from_numpy(lens).cuda(), SCALE, max_seq_len=int(lens.max()),
+                                       num_splits=splits, lse=lse, num_pages=npages + 1)
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy()
+        err = np.abs(o - ref)
+        bad_el = err > 2e-3 + 1e-2 * np.abs(ref)
+        assert not bad_el.any(), "splits=%d: %d outside tolerance (max err %.3g)" % (splits, int(bad_el.sum()), float(err.max()))
+        assert np.allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-4)
