@@ -938,25 +938,34 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
 
 // 8 INT4 codes of a dword (element e in bits 4 e) -> bf16(fma(code, S, Z)), S
 // scaled by kCodeScale as in code_pair
-__device__ __forceinline__ bf16x8 dq_int4x8(unsigned w, float S, float Z) {
+// Two code bytes (2 w, 2 w + 1 of x) as exact fp16 integers: the byte read
+// as an e4m3 value is code * 2^-9 (code_pair), and the scaled conversion
+// multiplies by its scale's power of two, 2^9.  With S and Z taken straight
+// from their packed fp16 pair, fma(code, S, Z) then needs no unpacking: the
+// fused multiply-add of fp16 operands into fp32 (v_fma_mix_f32) is exact in
+// the product and rounds the sum once, as fma(code, S, Z) in fp32 does.
+using h2 = _Float16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2 code_pair_h(unsigned x, int w) {
+  return w ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, false);
+}
+// canonical value of a code against the packed (S, Z) fp16 pair `sz`
+__device__ __forceinline__ float dq_h(_Float16 code, unsigned sz) {
+  const h2 p = __builtin_bit_cast(h2, sz);
+  return __builtin_fmaf((float)code, (float)p[0], (float)p[1]);
+}
+__device__ __forceinline__ bf16x8 dq_int4x8(unsigned w, unsigned sz) {
   const unsigned lo = mask_bytes(w, 0x0F0F0F0Fu);       // elements 0, 2, 4, 6
   const unsigned hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);  // elements 1, 3, 5, 7
-  const f32x2 l0 = code_pair(lo, 0), l1 = code_pair(lo, 1), h0 = code_pair(hi, 0), h1 = code_pair(hi, 1);
-  const u32x4 o = {pack_bf16x2(__builtin_fmaf(l0[0], S, Z), __builtin_fmaf(h0[0], S, Z)),
-                   pack_bf16x2(__builtin_fmaf(l0[1], S, Z), __builtin_fmaf(h0[1], S, Z)),
-                   pack_bf16x2(__builtin_fmaf(l1[0], S, Z), __builtin_fmaf(h1[0], S, Z)),
-                   pack_bf16x2(__builtin_fmaf(l1[1], S, Z), __builtin_fmaf(h1[1], S, Z))};
+  const h2 l0 = code_pair_h(lo, 0), l1 = code_pair_h(lo, 1), h0 = code_pair_h(hi, 0), h1 = code_pair_h(hi, 1);
+  const u32x4 o = {pack_bf16x2(dq_h(l0[0], sz), dq_h(h0[0], sz)), pack_bf16x2(dq_h(l0[1], sz), dq_h(h0[1], sz)),
+                   pack_bf16x2(dq_h(l1[0], sz), dq_h(h1[0], sz)), pack_bf16x2(dq_h(l1[1], sz), dq_h(h1[1], sz))};
   return __builtin_bit_cast(bf16x8, o);
 }
-
-// elements 8 hf .. 8 hf + 7 of 16 INT2 codes (element e in bits 2 e), given
-// b[j] = (w >> 2 j) & 0x03030303 (byte k of b[j] is element 4 k + j)
-__device__ __forceinline__ bf16x8 dq_int2x8(const unsigned (&b)[4], int hf, float S, float Z) {
-  const f32x2 f0 = code_pair(b[0], hf), f1 = code_pair(b[1], hf), f2 = code_pair(b[2], hf), f3 = code_pair(b[3], hf);
-  const u32x4 o = {pack_bf16x2(__builtin_fmaf(f0[0], S, Z), __builtin_fmaf(f1[0], S, Z)),
-                   pack_bf16x2(__builtin_fmaf(f2[0], S, Z), __builtin_fmaf(f3[0], S, Z)),
-                   pack_bf16x2(__builtin_fmaf(f0[1], S, Z), __builtin_fmaf(f1[1], S, Z)),
-                   pack_bf16x2(__builtin_fmaf(f2[1], S, Z), __builtin_fmaf(f3[1], S, Z))};
+__device__ __forceinline__ bf16x8 dq_int2x8(const unsigned (&b)[4], int hf, unsigned sz) {
+  const h2 f0 = code_pair_h(b[0], hf), f1 = code_pair_h(b[1], hf), f2 = code_pair_h(b[2], hf), f3 = code_pair_h(b[3], hf);
+  const u32x4 o = {pack_bf16x2(dq_h(f0[0], sz), dq_h(f1[0], sz)), pack_bf16x2(dq_h(f2[0], sz), dq_h(f3[0], sz)),
+                   pack_bf16x2(dq_h(f0[1], sz), dq_h(f1[1], sz)), pack_bf16x2(dq_h(f2[1], sz), dq_h(f3[1], sz))};
   return __builtin_bit_cast(bf16x8, o);
 }
 
@@ -1016,8 +1025,8 @@ template <> struct SubFill<kC4R4> {
   __device__ __forceinline__ unsigned sz_of(int ks, bool live) const {
     return live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u;
   }
-  __device__ __forceinline__ bf16x8 step(int ks, float S, float Z) {
-    return dq_int4x8(ks < 16 ? c[ks >> 2][ks & 3] : r[ks - 16], S, Z);
+  __device__ __forceinline__ bf16x8 step(int ks, unsigned sz) {
+    return dq_int4x8(ks < 16 ? c[ks >> 2][ks & 3] : r[ks - 16], sz);
   }
 };
 
@@ -1048,14 +1057,14 @@ template <> struct SubFill<kC2R4> {
     return live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u;
   }
   // k-step 4 m + d: half d & 1 of dword d / 2 of block m
-  __device__ __forceinline__ bf16x8 step(int ks, float S, float Z) {
-    if (ks >= 16) return dq_int4x8(r[ks - 16], S, Z);
+  __device__ __forceinline__ bf16x8 step(int ks, unsigned sz) {
+    if (ks >= 16) return dq_int4x8(r[ks - 16], sz);
     if ((ks & 1) == 0) {
       const unsigned w = c[ks >> 2][(ks & 3) >> 1];
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = mask_bytes(w >> (2 * j), 0x03030303u);
     }
-    return dq_int2x8(b, ks & 1, S, Z);
+    return dq_int2x8(b, ks & 1, sz);
   }
 };
 
@@ -1160,7 +1169,7 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   bf16x8 qall[18];
 #pragma unroll
   for (int d = 0; d < 18; ++d) qall[d] = *(const bf16x8*)(qlds + iw_chan(iw_ks(d), g));
-  float S0 = 0.0f, Z0 = 0.0f, S1 = 0.0f, Z1 = 0.0f;
+  unsigned SZ0 = 0u, SZ1 = 0u;  // (S, Z) fp16 pairs of the current group of each block
   bool live0 = false, live1 = false;
   auto qk_begin = [&](int u) {
     const bool ok = pg_next >= 0 && pg_next < a.num_pages;
@@ -1178,11 +1187,11 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
     constexpr bool kM = decltype(kMask)::value;
     const int ks = iw_ks(p);
     if (ks % 4 == 0 || ks == 16) {
-      sz_unpack(f0.sz_of(ks, !kM || live0), S0, Z0);
-      sz_unpack(f1.sz_of(ks, !kM || live1), S1, Z1);
+      SZ0 = f0.sz_of(ks, !kM || live0);
+      SZ1 = f1.sz_of(ks, !kM || live1);
     }
-    const bf16x8 k0 = f0.step(ks, S0, Z0);
-    const bf16x8 k1 = f1.step(ks, S1, Z1);
+    const bf16x8 k0 = f0.step(ks, SZ0);
+    const bf16x8 k1 = f1.step(ks, SZ1);
     const bf16x8 qk = qall[p];
     if (ks < 16) {
       __bf16* vw = (ks & 1) ? vw0o : vw0e;  // chunk iw_chan / 8 has the parity of ks
