@@ -99,21 +99,24 @@ __device__ __forceinline__ unsigned mask_bytes(unsigned w, unsigned m) {
   return r;
 }
 
-// Codes as floats, two per instruction: a code byte 0..15 read as an OCP fp8
-// e4m3 value is exactly code * 2^-9 (bytes 0..7 are the subnormals m * 2^-9,
-// 8..15 the normals (1 + m / 8) * 2^-6).  With the scale taken as S * 2^9
-// (exact for every fp16 S) the product is code * S exactly, so
-// fma(code * 2^-9, S * 2^9, Z) rounds the same sum as fma(code, S, Z).
-constexpr float kCodeScale = 512.0f;
-// bytes 2 w and 2 w + 1 of x as floats (code * 2^-9); w is a literal after unrolling
-__device__ __forceinline__ f32x2 code_pair(unsigned x, int w) {
-  return w ? __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+// Codes as exact fp16 integers, two per instruction: a code byte 0..15 read
+// as an OCP fp8 e4m3 value is exactly code * 2^-9 (bytes 0..7 are the
+// subnormals m * 2^-9, 8..15 the normals (1 + m / 8) * 2^-6), and the scaled
+// conversion multiplies by the power of two of its scale, here 2^9 (bytes 2 w
+// and 2 w + 1 of x; w is a literal after unrolling).  With S and Z taken
+// straight from their packed fp16 pair, fma(code, S, Z) needs no unpacking:
+// the fused multiply-add of fp16 operands into fp32 (v_fma_mix_f32) is exact
+// in the product (11 x 4 significant bits) and rounds the sum once, as
+// fma(code, S, Z) in fp32 does.
+using h2 = _Float16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2 code_pair_h(unsigned x, int w) {
+  return w ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, false);
 }
-
-// S (scaled by kCodeScale, see code_pair) and Z of a packed fp16 pair
-__device__ __forceinline__ void sz_unpack(unsigned sz, float& S, float& Z) {
-  S = half_bits_to_f32(sz) * kCodeScale;
-  Z = half_bits_to_f32(sz >> 16);
+// canonical value of a code against the packed (S, Z) fp16 pair `sz`
+__device__ __forceinline__ float dq_h(_Float16 code, unsigned sz) {
+  const h2 p = __builtin_bit_cast(h2, sz);
+  return __builtin_fmaf((float)code, (float)p[0], (float)p[1]);
 }
 
 // ---------------------------------------------------------------- tile fills
@@ -144,8 +147,8 @@ template <> struct Fill<kC4R4> {
   bool ok;
   // working state of the dword being converted
   unsigned lo, hi, outw[4];
-  f32x2 flo, fhi;
-  float S, Z;
+  h2 flo, fhi;
+  unsigned szv;  // the dword's (S, Z) fp16 pair
   const uint8_t* base;  // page of the pending tile
   int hp;               // its half of the page
   static constexpr int kLoads = 6;
@@ -177,16 +180,16 @@ template <> struct Fill<kC4R4> {
     if (q == 0) {
       const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
       const unsigned w = p < 8 ? c[p >> 2][p & 3] : r;
-      sz_unpack(live ? (p < 8 ? sz[p >> 2] : rsz) : 0u, S, Z);
+      szv = live ? (p < 8 ? sz[p >> 2] : rsz) : 0u;
       lo = mask_bytes(w, 0x0F0F0F0Fu);        // elements 0, 2, 4, 6
       hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);   // elements 1, 3, 5, 7
     }
     if ((q & 1) == 0) {  // bytes q, q + 1 of lo / hi: elements 2q, 2q + 2 / 2q + 1, 2q + 3
-      flo = code_pair(lo, q >> 1);
-      fhi = code_pair(hi, q >> 1);
+      flo = code_pair_h(lo, q >> 1);
+      fhi = code_pair_h(hi, q >> 1);
     }
-    const float a = __builtin_fmaf(flo[q & 1], S, Z);
-    const float b = __builtin_fmaf(fhi[q & 1], S, Z);
+    const float a = dq_h(flo[q & 1], szv);
+    const float b = dq_h(fhi[q & 1], szv);
     outw[q] = pack_bf16x2(a, b);
     if (q == 3) {
       const int chunk = p < 8 ? 4 * (cs + 8 * (p >> 2)) + (p & 3) : 64 + cs;
@@ -207,8 +210,8 @@ template <> struct Fill<kC2R4> {
   unsigned r, rsz;
   bool ok;
   unsigned b0, b1, b2, b3, outw[4];
-  f32x2 f0, f1, f2, f3;
-  float S, Z;
+  h2 f0, f1, f2, f3;
+  unsigned szv;  // the dword's (S, Z) fp16 pair
   const uint8_t* base;  // page of the pending tile
   int hp;               // its half of the page
   static constexpr int kLoads = 5;
@@ -240,7 +243,7 @@ template <> struct Fill<kC2R4> {
     if (u < 32) {
       const int v = u >> 3, q = u & 7;
       if (q == 0) {
-        sz_unpack(live ? sz[v >> 1] : 0u, S, Z);
+        szv = live ? sz[v >> 1] : 0u;
         const unsigned w = c[v];
         // byte k of (w >> 2j) & 0x03030303 holds element 4k + j
         b0 = mask_bytes(w, 0x03030303u);
@@ -253,31 +256,31 @@ template <> struct Fill<kC2R4> {
       // q % 4 = 0 (b0, b1) and 1 (b2, b3) and serve pairs q and q + 2
       const int k = q >> 1;
       if ((q & 3) == 0) {
-        f0 = code_pair(b0, q >> 2);
-        f1 = code_pair(b1, q >> 2);
+        f0 = code_pair_h(b0, q >> 2);
+        f1 = code_pair_h(b1, q >> 2);
       }
       if ((q & 3) == 1) {
-        f2 = code_pair(b2, q >> 2);
-        f3 = code_pair(b3, q >> 2);
+        f2 = code_pair_h(b2, q >> 2);
+        f3 = code_pair_h(b3, q >> 2);
       }
-      const float ea = __builtin_fmaf((q & 1) ? f2[k & 1] : f0[k & 1], S, Z);
-      const float eb = __builtin_fmaf((q & 1) ? f3[k & 1] : f1[k & 1], S, Z);
+      const float ea = dq_h((q & 1) ? f2[k & 1] : f0[k & 1], szv);
+      const float eb = dq_h((q & 1) ? f3[k & 1] : f1[k & 1], szv);
       outw[q & 3] = pack_bf16x2(ea, eb);
       if ((q & 3) == 3)
         *(u32x4*)(row + 8 * (8 * cs + 2 * v + (q >> 2))) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
     } else {
       const int q = u - 32;
       if (q == 0) {
-        sz_unpack(live ? rsz : 0u, S, Z);
+        szv = live ? rsz : 0u;
         b0 = mask_bytes(r, 0x0F0F0F0Fu);
         b1 = mask_bytes(r >> 4, 0x0F0F0F0Fu);
       }
       if ((q & 1) == 0) {
-        f0 = code_pair(b0, q >> 1);
-        f1 = code_pair(b1, q >> 1);
+        f0 = code_pair_h(b0, q >> 1);
+        f1 = code_pair_h(b1, q >> 1);
       }
-      const float ea = __builtin_fmaf(f0[q & 1], S, Z);
-      const float eb = __builtin_fmaf(f1[q & 1], S, Z);
+      const float ea = dq_h(f0[q & 1], szv);
+      const float eb = dq_h(f1[q & 1], szv);
       outw[q] = pack_bf16x2(ea, eb);
       if (q == 3) *(u32x4*)(row + 8 * (64 + cs)) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
     }
@@ -936,24 +939,8 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
   return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), m));
 }
 
-// 8 INT4 codes of a dword (element e in bits 4 e) -> bf16(fma(code, S, Z)), S
-// scaled by kCodeScale as in code_pair
-// Two code bytes (2 w, 2 w + 1 of x) as exact fp16 integers: the byte read
-// as an e4m3 value is code * 2^-9 (code_pair), and the scaled conversion
-// multiplies by its scale's power of two, 2^9.  With S and Z taken straight
-// from their packed fp16 pair, fma(code, S, Z) then needs no unpacking: the
-// fused multiply-add of fp16 operands into fp32 (v_fma_mix_f32) is exact in
-// the product and rounds the sum once, as fma(code, S, Z) in fp32 does.
-using h2 = _Float16 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ h2 code_pair_h(unsigned x, int w) {
-  return w ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, true)
-           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, false);
-}
-// canonical value of a code against the packed (S, Z) fp16 pair `sz`
-__device__ __forceinline__ float dq_h(_Float16 code, unsigned sz) {
-  const h2 p = __builtin_bit_cast(h2, sz);
-  return __builtin_fmaf((float)code, (float)p[0], (float)p[1]);
-}
+// 8 INT4 codes of a dword (element e in bits 4 e) -> bf16(fma(code, S, Z)),
+// (S, Z) the packed fp16 pair `sz`
 __device__ __forceinline__ bf16x8 dq_int4x8(unsigned w, unsigned sz) {
   const unsigned lo = mask_bytes(w, 0x0F0F0F0Fu);       // elements 0, 2, 4, 6
   const unsigned hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);  // elements 1, 3, 5, 7
