@@ -90,9 +90,10 @@ __device__ __forceinline__ float wave_partner(float v) {
 
 // ---------------------------------------------------------------- dequantization
 
-// w & m, opaque to the optimizer: keeps the byte-wise conversions below as
-// v_cvt_f32_ubyte{0..3} on the masked word instead of one bitfield extract
-// per element.
+// w & m, opaque to the optimizer: keeps one AND per word ahead of the
+// two-byte conversions below (a plain & lets the compiler rewrite the
+// mask-and-convert sequence into more instructions: +36 per tile in the
+// <= 16-row loop).
 __device__ __forceinline__ unsigned mask_bytes(unsigned w, unsigned m) {
   unsigned r;
   asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
