@@ -591,9 +591,9 @@ __device__ __forceinline__ void split_pass_fill_only(const DecodeArgs& a, __bf16
 // LDS, which every wavefront of the group then reads; the denominators and
 // maxima of the quarters are combined at the end of the pass, so all
 // wavefronts of a group hold bitwise the same weights and denominator.  The
-// packed bytes of the next D tiles are kept in registers: D = 1 (the other
-// workgroup on the compute unit covers the load latency), except with the
-// packed P.V of <= 16 rows, whose shorter tile wants D = 2.
+// packed bytes of the next D tiles are kept in registers (the launcher uses
+// D = 1: at C = 4 the other workgroup on the compute unit covers the load
+// latency).
 template <int C> struct CsAcc {
   f32x16 o[16 / C];
   float l_sum, m_ref, m_seen;
@@ -601,7 +601,7 @@ template <int C> struct CsAcc {
 
 constexpr int kXchFloats = 64 * 16;  // one wavefront's partial S^T block
 
-template <int F, int C, int D, bool kPk>
+template <int F, int C, int D>
 __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int k0,
                                               int k1, const bf16x8 (&qr)[36 / C], int limit, bool fixed,
                                               float m_fixed, CsAcc<C>& acc) {
@@ -741,22 +741,16 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
       __syncthreads();  // weights published; every wavefront is past its exchange reads
       // ---- O^T (this part's channels) += khat^T . P, next tile's dequant between the MFMAs
       const int nvalid_next = min(kTileTok, L - (k + 1) * kTileTok);
-      // packed (<= 16 rows): operand column n < 16 holds the high weights of
-      // row n and column n + 16 its low weights, so one MFMA per step adds both
-      // halves into two accumulator columns, summed when the pass is written
-      constexpr int kPvH = kPk ? 1 : 2;  // P.V MFMAs per step
+      constexpr int kPvH = 2;  // P.V MFMAs per step: high and low weights
       constexpr int kSub = Fill<F>::kSubsteps;
       constexpr int kSlots = 2 * kPvH * NCT;                 // MFMAs of this phase
       constexpr int kPer = kSub ? (kSub + kSlots - 1) / kSlots : 1;  // dequant steps per MFMA slot
       constexpr int kFirst = kSlots - (kSub + kPer - 1) / kPer;     // first slot that carries steps
       bf16x8 bp[2][kPvH];
-      {
-        const int src = kPk ? ((lane & 32) | (lane & 15)) : lane, hsel = kPk ? (lane >> 4) & 1 : 0;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int h = 0; h < kPvH; ++h) bp[kk][h] = *(const bf16x8*)(pbuf + (2 * kk + h + hsel) * 1024 + 16 * src);
-      }
+        for (int h = 0; h < kPvH; ++h) bp[kk][h] = *(const bf16x8*)(pbuf + (2 * kk + h) * 1024 + 16 * lane);
       const __bf16* vbase = tile + tr_row0 * kRow + 8 * tr_chunk + tr_half + 32 * (part * NCT);
       auto tr_read = [&](int step) {  // step = NCT kk + ct (ct relative to this part)
         const __bf16* v0 = vbase + 16 * (step / NCT) * kRow + 32 * (step % NCT);
@@ -814,16 +808,10 @@ __device__ __forceinline__ bool split_pass_cs(const DecodeArgs& a, __bf16* smem,
   return lifted;
 }
 
-template <bool kDirect, int C, bool kPk>
+template <bool kDirect, int C>
 __device__ __forceinline__ void write_split_cs(const DecodeArgs& a, int b, int64_t slot, const RowOf& row,
                                                CsAcc<C>& acc) {
   constexpr int NCT = 16 / C;
-  if (kPk) {  // packed P.V: row n's output is accumulator column n plus column n + 16
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc.o[ct][i] += __shfl_xor(acc.o[ct][i], 16);
-  }
   const int hi = (threadIdx.x & 63) >> 5, part = (threadIdx.x >> 6) % C;
   const float l_tot = acc.l_sum + wave_partner(acc.l_sum);
   // a row that sees no token of the piece: output 0, lse -inf
@@ -1464,25 +1452,12 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, __bf16* smem,
     }
     bool fixed = false;
     float m_fixed = 0.0f;
-    if (C == 4 && rows <= 16) {
-      for (int pass = 0;; ++pass) {
-        CsAcc<C> acc;
-        const bool lifted = split_pass_cs<F, C, 2, true>(a, smem, bt, L, k0, k1, qr, row.limit, fixed, m_fixed, acc);
-        const bool redo = __syncthreads_or(lifted);
-        if (!redo || pass > 0) {
-          write_split_cs<kDirect, C, true>(a, b, slot, row, acc);
-          return;
-        }
-        fixed = true;
-        m_fixed = acc.m_seen;
-      }
-    }
     for (int pass = 0;; ++pass) {
       CsAcc<C> acc;
-      const bool lifted = split_pass_cs<F, C, 1, false>(a, smem, bt, L, k0, k1, qr, row.limit, fixed, m_fixed, acc);
+      const bool lifted = split_pass_cs<F, C, 1>(a, smem, bt, L, k0, k1, qr, row.limit, fixed, m_fixed, acc);
       const bool redo = __syncthreads_or(lifted);
       if (!redo || pass > 0) {
-        write_split_cs<kDirect, C, false>(a, b, slot, row, acc);
+        write_split_cs<kDirect, C>(a, b, slot, row, acc);
         return;
       }
       fixed = true;
