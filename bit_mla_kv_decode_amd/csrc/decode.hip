@@ -88,6 +88,26 @@ __device__ __forceinline__ float wave_partner(float v) {
   return __builtin_bit_cast(float, other);
 }
 
+// Q.K^T logits accumulated in VGPRs.  Beside the 256 O accumulators of the
+// > 64-row kernel (all AGPRs) the compiler gives a builtin MFMA chain an AGPR
+// destination as well and swaps one O block through VGPRs around every tile
+// (48 accumulator moves per tile, plus 16 more to read the logits out).
+// Written as inline asm with VGPR operands the chain needs none.  The compiler
+// does not see the matrix-pipe hazards of asm, so each MFMA is issued two wait
+// states after whatever precedes it (a VALU write of an operand needs them) and
+// the chain ends with 24 wait states, more than a 32x32 MFMA needs before a
+// VALU instruction reads or overwrites its result; a dependent MFMA reading
+// the previous one's result as its accumulator may follow at once.
+__device__ __forceinline__ void mfma_v_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_drain(f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+}
+
 // ---------------------------------------------------------------- dequantization
 
 // w & m, opaque to the optimizer: keeps one AND per word ahead of the
@@ -444,10 +464,11 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
     fill.begin(a.cache, win.page_of(kn), kn & 1, a.num_pages);
     constexpr int kLoadEvery = 3;
 
-    // ---- S^T = khat . q^T for the 32 tokens of the tile.  Operands are read
-    //      4 k-steps ahead; scheduling barriers pin that order so LDS latency
-    //      hides behind the MFMAs instead of stalling each one.
-    f32x16 s = {};
+    // ---- S^T = khat . q^T for the 32 tokens of the tile (in VGPRs, see
+    //      mfma_v_first).  Operands are read 4 k-steps ahead; scheduling
+    //      barriers pin that order so LDS latency hides behind the MFMAs
+    //      instead of stalling each one.
+    f32x16 s;
     const __bf16* arow = tile + rho(lane & 31) * kRow + 8 * hi;
     bf16x8 kv[4], qv[2];
 #pragma unroll
@@ -458,12 +479,16 @@ __device__ __forceinline__ bool split_pass(const DecodeArgs& a, __bf16* smem, co
     for (int ks = 0; ks < 36; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
       const bf16x8 bq = q_in_lds(ks) ? qv[(ks >> 1) & 1] : qr[q_in_lds(ks) ? 0 : q_reg_index(ks)];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks & 3], bq, s, 0, 0, 0);
+      if (ks == 0)
+        mfma_v_first(s, kv[0], bq);
+      else
+        mfma_v_acc(s, kv[ks & 3], bq);
       __builtin_amdgcn_sched_barrier(0);
       if (ks + 4 < 36) kv[ks & 3] = *(const bf16x8*)(arow + 16 * (ks + 4));
       if (q_in_lds(ks) && ks + 4 < 32) qv[(ks >> 1) & 1] = *(const bf16x8*)(qrow + 16 * ((ks >> 1) + 2));
       if (ks % kLoadEvery == 1 && ks / kLoadEvery < Fill<F>::kLoads) fill.issue(ks / kLoadEvery);
     }
+    mfma_v_drain(s);
     __builtin_amdgcn_sched_barrier(0);
     // ---- softmax weights (log2 domain); reg r is token 8 (r / 4) + 4 hi + r % 4
     if ((k + 1) * kTileTok > limit_min) {  // the last tokens: the row's limit (and the sequence end)
