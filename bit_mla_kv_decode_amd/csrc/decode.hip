@@ -942,9 +942,8 @@ constexpr int kIwThreads = 64 * kIwWaves;
 constexpr int kIwTok = 32;                        // tokens per tile of a wavefront
 constexpr int kVRow = kDc + 16;                   // bf16 per row of a V buffer (1056 bytes; see vrow)
 constexpr int kVBuf = kIwTok * kVRow;             // bf16 per wavefront buffer
-constexpr int kIwQRow = kD + 8;                   // bf16 per staged q row (1168 bytes)
 constexpr int kIwRedRow = kDc + 4;                // fp32 per row in the end-of-piece merge
-constexpr size_t kIwRedOff = ((size_t)kIwWaves * kVBuf + 16 * kIwQRow) * sizeof(__bf16);  // 153856 bytes
+constexpr size_t kIwRedOff = (size_t)kIwWaves * kVBuf * sizeof(__bf16);  // 135168 bytes
 static_assert(kIwWaves * 16 * kIwRedRow * sizeof(float) <= (size_t)kIwWaves * kVBuf * sizeof(__bf16),
               "the wavefronts' outputs fit in the V buffers");
 
@@ -1104,8 +1103,8 @@ __device__ __forceinline__ constexpr int pv_end(int p) { return p < 2 ? 4 * p + 
 // overflowed (a logit more than kMaxLift above the reference): the caller
 // redoes the piece with a fixed reference.
 template <int F>
-__device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, int L, int u0, int u1,
-                                        int limit, bool fixed, float m_fixed, IwAcc& acc) {
+__device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const int32_t* bt, const __bf16* qg, int L,
+                                        int u0, int u1, int limit, bool fixed, float m_fixed, IwAcc& acc) {
   using SF = SubFill<F>;
   const int limit_min = L - (a.s_q - 1);
   // the wavefront index as a scalar: tile indices, page offsets and load
@@ -1113,7 +1112,6 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int t = lane & 15, g = lane >> 4;  // QK operand lane: token t, channel quarter g; S^T lane: row t, tokens 4 g..
   __bf16* __restrict__ vbuf = smem + wave * kVBuf;
-  const __bf16* __restrict__ qlds = smem + kIwWaves * kVBuf + t * kIwQRow;
 #pragma unroll
   for (int ct = 0; ct < 32; ++ct) acc.o[ct] = (f32x4){};
   acc.l_sum = 0.0f;
@@ -1166,10 +1164,12 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   // ---- Q.K^T state of the tile being dequantized
   f32x4 s0, s1;
   // the q operand of every k-step stays in registers for the pass (72 of
-  // them: one wavefront per SIMD leaves room), read from LDS once
+  // them: one wavefront per SIMD leaves room), loaded once from global
+  // memory behind the first tile's loads, so both latencies overlap (qg: the
+  // lane's q row, null for a row without a head: zeros)
   bf16x8 qall[18];
 #pragma unroll
-  for (int d = 0; d < 18; ++d) qall[d] = *(const bf16x8*)(qlds + iw_chan(iw_ks(d), g));
+  for (int d = 0; d < 18; ++d) qall[d] = qg ? *(const bf16x8*)(qg + iw_chan(iw_ks(d), g)) : (bf16x8){};
   unsigned SZ0 = 0u, SZ1 = 0u;  // (S, Z) fp16 pairs of the current group of each block
   bool live0 = false, live1 = false;
   auto qk_begin = [&](int u) {
@@ -1301,7 +1301,7 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
 struct IwRed {
   float m[kIwWaves][16], l[kIwWaves][16], s[kIwWaves][16];
 };
-// V buffers, staged q, then the merge record
+// V buffers, then the merge record
 constexpr size_t kIwLds = kIwRedOff + sizeof(IwRed);
 
 // Per-row totals of the piece: every lane of row t (lanes t, t + 16, t + 32,
@@ -1404,25 +1404,15 @@ __device__ __forceinline__ void process_range_iw(const DecodeArgs& a, __bf16* sm
     __threadfence();
   }
   __syncthreads();  // the previous piece (if any) has finished with LDS
-  {  // stage q of the piece's rows (zeros for rows without a head)
-    __bf16* ql = smem + kIwWaves * kVBuf;
-    for (int ci = tid; ci < 16 * (kD / 8); ci += kIwThreads) {
-      const int r = ci / (kD / 8), c = ci % (kD / 8);
-      const RowOf qrow = row_of(a, chunk, L, r);
-      bf16x8 v = {};
-      if (r < rows && qrow.valid) v = *(const bf16x8*)(a.q + ((int64_t)b * R + qrow.g) * kD + 8 * c);
-      *(bf16x8*)(ql + r * kIwQRow + 8 * c) = v;
-    }
-  }
-  __syncthreads();
   const RowOf row = row_of(a, chunk, L, lane & 15);
+  const __bf16* qg = (lane & 15) < rows && row.valid ? a.q + ((int64_t)b * R + row.g) * kD : nullptr;
   const int limit = min(row.limit, L);
   const int u1 = min(k1, (L + kIwTok - 1) / kIwTok);
   bool fixed = false;
   float m_fixed = 0.0f;
   for (int pass = 0;; ++pass) {
     IwAcc acc;
-    const bool lifted = iw_pass<F>(a, smem, bt, L, k0, u1, limit, fixed, m_fixed, acc);
+    const bool lifted = iw_pass<F>(a, smem, bt, qg, L, k0, u1, limit, fixed, m_fixed, acc);
     const bool redo = __syncthreads_or(lifted);
     float M, Ltot, seen, f_own;
     iw_totals(red, acc, M, Ltot, seen, f_own);
