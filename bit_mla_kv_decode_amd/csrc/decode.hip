@@ -1763,6 +1763,9 @@ __global__ __launch_bounds__(decode_threads<C>(), C == 4 ? 2 : 1) void k_decode_
 // slot per lane (wavefront max and sum) and kept in LDS; the rows of eight
 // slots are then in flight at a time, and rows of zero weight (empty pieces,
 // lse = -inf, whose rows may hold anything) are never read.
+// the balanced merge uses NC = 1 while its 8 H B wavefronts are at most
+// two per SIMD (a few long sequences: many slots each, few rows)
+constexpr int kCombineNarrowWaves = 2048;
 constexpr int kCombineMaxSlots = 512;  // slots of one sequence: <= 64 splits or <= 512 balanced shares
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -1777,10 +1780,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Rows of one (sequence, head): wavefront `part` of the head's 8 / NC
+// wavefronts owns channels [64 NC part, 64 NC (part + 1)), NC per lane; the
+// weights are computed by every wavefront (the log-sum-exps are few and hit
+// in L2).  The rows of 32 / NC slots are in flight at a time: NC = 1 keeps
+// the loads of a few dozen slots in one round when the rows are few and the
+// merge is latency-bound, NC = 4 streams 16-byte loads when they are many.
+template <int NC>
 __device__ __forceinline__ void combine_rows(const float* __restrict__ o_part, const float* __restrict__ lse_part,
-                                             int64_t first, int count, int64_t b, int H, int head, int half,
+                                             int64_t first, int count, int64_t b, int H, int head, int part,
                                              float* __restrict__ wbuf, __bf16* __restrict__ out,
                                              float* __restrict__ lse_out) {
+  using vec = float __attribute__((ext_vector_type(NC)));
+  constexpr int U = 32 / NC;  // slots per round
   const int lane = threadIdx.x & 63;
   // a sequence has at most kCombineMaxSlots pieces; the clamp only keeps LDS
   // accesses in bounds for a workspace the decode did not write
@@ -1804,27 +1816,33 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ o_part, c
     }
     W = wave_sum(W);
   }
-  f32x4 acc = {};
+  const int ch = 64 * NC * part + NC * lane;
+  vec acc = {};
   if (M != -INFINITY) {
-    const float* base = o_part + (first * H + head) * kDc + 256 * half + 4 * lane;
-    for (int s0 = 0; s0 < count; s0 += 8) {
-      float w[8];
-      f32x4 x[8];
+    const float* base = o_part + (first * H + head) * kDc + ch;
+    for (int s0 = 0; s0 < count; s0 += U) {
+      float w[U];
+      vec x[U];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < U; ++j) {
         w[j] = s0 + j < count ? wbuf[s0 + j] : 0.0f;  // same address in every lane: a broadcast read
-        x[j] = (f32x4){};
-        if (w[j] > 0.0f) x[j] = *(const f32x4*)(base + (int64_t)(s0 + j) * H * kDc);  // uniform
+        x[j] = (vec){};
+        if (w[j] > 0.0f) x[j] = *(const vec*)(base + (int64_t)(s0 + j) * H * kDc);  // uniform
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc += w[j] * x[j];
+      for (int j = 0; j < U; ++j) acc += w[j] * x[j];
     }
   }
   const float inv = (M != -INFINITY) ? 1.0f / W : 0.0f;
   acc *= inv;
-  const u32x2 packed = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-  *(u32x2*)(out + (b * H + head) * kDc + 256 * half + 4 * lane) = packed;
-  if (lse_out && half == 0 && lane == 0) lse_out[b * H + head] = (M != -INFINITY) ? M + logf(W) : -INFINITY;
+  __bf16* o = out + (b * H + head) * kDc + ch;
+  if constexpr (NC == 4) {
+    *(u32x2*)o = (u32x2){pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  } else {
+    static_assert(NC == 1, "one or four channels per lane");
+    *o = (__bf16)acc[0];
+  }
+  if (lse_out && part == 0 && lane == 0) lse_out[b * H + head] = (M != -INFINITY) ? M + logf(W) : -INFINITY;
 }
 
 // per-sequence splits: rows (b * S + s) * H + head
@@ -1834,19 +1852,22 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_par
   const int b = blockIdx.y, wave = threadIdx.x >> 6;
   const int head = blockIdx.x * 2 + (wave >> 1);
   if (head >= H) return;
-  combine_rows(o_part, lse_part, (int64_t)b * S, S, b, H, head, wave & 1, wbuf[wave], out, lse_out);
+  combine_rows<4>(o_part, lse_part, (int64_t)b * S, S, b, H, head, wave & 1, wbuf[wave], out, lse_out);
 }
 
 // balanced partition: slots [meta[2b], meta[2b] + meta[2b + 1]) of sequence b
 // (an empty sequence has count 0: output 0, lse -inf)
+template <int NC>
 __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, const int* __restrict__ meta,
                                                       int H, __bf16* __restrict__ out, float* __restrict__ lse_out) {
   __shared__ float wbuf[4][kCombineMaxSlots];
+  constexpr int P = 8 / NC;  // wavefronts per head
   const int b = blockIdx.y, wave = threadIdx.x >> 6;
-  const int head = blockIdx.x * 2 + (wave >> 1);
+  const int gw = blockIdx.x * 4 + wave;
+  const int head = gw / P;
   if (head >= H) return;
-  combine_rows(o_part, lse_part, meta[2 * b], meta[2 * b + 1], b, H, head, wave & 1, wbuf[wave], out, lse_out);
+  combine_rows<NC>(o_part, lse_part, meta[2 * b], meta[2 * b + 1], b, H, head, gw % P, wbuf[wave], out, lse_out);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1959,8 +1980,12 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int batch,
 
 hipError_t launch_combine_flat(const float* o_part, const float* lse_part, const int* meta, int batch, int heads,
                                __bf16* out, float* lse_out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_combine_flat, dim3((heads + 1) / 2, batch), dim3(256), 0, stream, o_part, lse_part, meta,
-                     heads, out, lse_out);
+  if (8ll * heads * batch <= kCombineNarrowWaves)
+    hipLaunchKernelGGL(k_combine_flat<1>, dim3(2 * heads, batch), dim3(256), 0, stream, o_part, lse_part, meta,
+                       heads, out, lse_out);
+  else
+    hipLaunchKernelGGL(k_combine_flat<4>, dim3((heads + 1) / 2, batch), dim3(256), 0, stream, o_part, lse_part,
+                       meta, heads, out, lse_out);
   return hipGetLastError();
 }
 
