@@ -110,34 +110,53 @@ __device__ __forceinline__ void mfma_v_drain(f32x16& d) {
 
 // ---------------------------------------------------------------- dequantization
 
-// w & m, opaque to the optimizer: keeps one AND per word ahead of the
-// two-byte conversions below (a plain & lets the compiler rewrite the
-// mask-and-convert sequence into more instructions: +36 per tile in the
-// <= 16-row loop).
+// w & m, opaque to the optimizer: keeps one AND per masked word (a plain &
+// lets the compiler rewrite the mask-and-convert sequence into more
+// instructions).
 __device__ __forceinline__ unsigned mask_bytes(unsigned w, unsigned m) {
   unsigned r;
   asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
   return r;
 }
 
-// Codes as exact fp16 integers, two per instruction: a code byte 0..15 read
-// as an OCP fp8 e4m3 value is exactly code * 2^-9 (bytes 0..7 are the
-// subnormals m * 2^-9, 8..15 the normals (1 + m / 8) * 2^-6), and the scaled
-// conversion multiplies by the power of two of its scale, here 2^9 (bytes 2 w
-// and 2 w + 1 of x; w is a literal after unrolling).  With S and Z taken
-// straight from their packed fp16 pair, fma(code, S, Z) needs no unpacking:
-// the fused multiply-add of fp16 operands into fp32 (v_fma_mix_f32) is exact
-// in the product (11 x 4 significant bits) and rounds the sum once, as
-// fma(code, S, Z) in fp32 does.
 using h2 = _Float16 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ h2 code_pair_h(unsigned x, int w) {
-  return w ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, true)
-           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, false);
+
+// Codes with no conversion instruction at all: a code c alone in bits
+// [k, k + b) of a 16-bit half (k + b <= 10, the other bits zero) is the fp16
+// subnormal c 2^(k - 24), exact.  v_fma_mix_f32 takes it as one operand, S
+// 2^(24 - k) in fp32 as the other (exact: S has 11 significant bits) and Z
+// from the packed pair: the product is c S exactly and the sum is rounded
+// once, i.e. fma(code, S, Z) in fp32.  SzScaled<N> holds S 2^(24 - k) for the
+// N bit offsets k = 0, b, 2b, .. a format uses (4-bit codes at k = 0, 4;
+// 2-bit codes at k = 0, 2, 4, 6) and the pair, whose Z half is read as is.
+template <int N> struct SzScaled {
+  float s[N];
+  unsigned sz;
+};
+template <int N, int kBits>
+__device__ __forceinline__ SzScaled<N> sz_scaled(unsigned sz) {
+  const float S = (float)__builtin_bit_cast(h2, sz)[0];
+  SzScaled<N> r;
+#pragma unroll
+  for (int i = 0; i < N; ++i) r.s[i] = S * (float)(1 << (24 - kBits * i));
+  r.sz = sz;
+  return r;
 }
-// canonical value of a code against the packed (S, Z) fp16 pair `sz`
-__device__ __forceinline__ float dq_h(_Float16 code, unsigned sz) {
-  const h2 p = __builtin_bit_cast(h2, sz);
-  return __builtin_fmaf((float)code, (float)p[0], (float)p[1]);
+__device__ __forceinline__ float dq_sub(_Float16 c, float s, unsigned sz) {
+  return __builtin_fmaf((float)c, s, (float)__builtin_bit_cast(h2, sz)[1]);
+}
+__device__ __forceinline__ h2 as_h2(unsigned w) { return __builtin_bit_cast(h2, w); }
+
+// 2-bit codes: element e of a dword sits at bit 2 e; m[j] (j < 4) keeps
+// elements j and j + 8 in place (bits 2 j and 16 + 2 j), m[j] (j >= 4) the
+// same of the dword shifted right by 8.  Half hf of m[j] gives element 8 hf +
+// j, against scale j % 4 (2^(24 - 2 (j % 4)) S).
+__device__ __forceinline__ void int2_split(unsigned w, unsigned (&m)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m[j] = mask_bytes(w, 0x00030003u << (2 * j));
+  const unsigned w8 = w >> 8;
+#pragma unroll
+  for (int j = 4; j < 8; ++j) m[j] = mask_bytes(w8, 0x00030003u << (2 * (j - 4)));
 }
 
 // ---------------------------------------------------------------- tile fills
@@ -166,10 +185,10 @@ template <> struct Fill<kC4R4> {
   unsigned sz[2];
   unsigned r, rsz;
   bool ok;
-  // working state of the dword being converted
-  unsigned lo, hi, outw[4];
-  h2 flo, fhi;
-  unsigned szv;  // the dword's (S, Z) fp16 pair
+  // working state of the dword being converted: its elements split as
+  // dq_int4x8 does, and the (S, Z) of its group (see SzScaled)
+  unsigned ma, mb, mc, md, outw[4];
+  SzScaled<2> zs;
   const uint8_t* base;  // page of the pending tile
   int hp;               // its half of the page
   static constexpr int kLoads = 6;
@@ -199,18 +218,20 @@ template <> struct Fill<kC4R4> {
     const int l = threadIdx.x & 31, t = rho(l), cs = threadIdx.x >> 5;  // token rho(l) lives in row l
     const int p = u >> 2, q = u & 3;
     if (q == 0) {
-      const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
+      if ((p & 3) == 0) {  // a new group: content dwords 0 and 4, the RoPE dword
+        const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
+        zs = sz_scaled<2, 4>(live ? (p < 8 ? sz[p >> 2] : rsz) : 0u);
+      }
       const unsigned w = p < 8 ? c[p >> 2][p & 3] : r;
-      szv = live ? (p < 8 ? sz[p >> 2] : rsz) : 0u;
-      lo = mask_bytes(w, 0x0F0F0F0Fu);        // elements 0, 2, 4, 6
-      hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);   // elements 1, 3, 5, 7
+      ma = mask_bytes(w, 0x000F000Fu);        // elements 0, 4 (2^24 S)
+      mb = mask_bytes(w, 0x00F000F0u);        // elements 1, 5 (2^20 S)
+      mc = mask_bytes(w >> 8, 0x000F000Fu);   // elements 2, 6
+      md = mask_bytes(w >> 8, 0x00F000F0u);   // elements 3, 7
     }
-    if ((q & 1) == 0) {  // bytes q, q + 1 of lo / hi: elements 2q, 2q + 2 / 2q + 1, 2q + 3
-      flo = code_pair_h(lo, q >> 1);
-      fhi = code_pair_h(hi, q >> 1);
-    }
-    const float a = dq_h(flo[q & 1], szv);
-    const float b = dq_h(fhi[q & 1], szv);
+    // pair q: elements 2q, 2q + 1 = half q / 2 of (ma, mb) (q even) or (mc, md)
+    const int hf = q >> 1;
+    const float a = dq_sub(as_h2((q & 1) ? mc : ma)[hf], zs.s[0], zs.sz);
+    const float b = dq_sub(as_h2((q & 1) ? md : mb)[hf], zs.s[1], zs.sz);
     outw[q] = pack_bf16x2(a, b);
     if (q == 3) {
       const int chunk = p < 8 ? 4 * (cs + 8 * (p >> 2)) + (p & 3) : 64 + cs;
@@ -230,9 +251,8 @@ template <> struct Fill<kC2R4> {
   unsigned sz[2];
   unsigned r, rsz;
   bool ok;
-  unsigned b0, b1, b2, b3, outw[4];
-  h2 f0, f1, f2, f3;
-  unsigned szv;  // the dword's (S, Z) fp16 pair
+  unsigned ma, mb, mc, md, outl[4], outh[4];  // masked words; packed pairs of both halves
+  SzScaled<4> zs;  // (S, Z) of the group: 2^24 S, 2^22 S, 2^20 S, 2^18 S (RoPE: s[0], s[2])
   const uint8_t* base;  // page of the pending tile
   int hp;               // its half of the page
   static constexpr int kLoads = 5;
@@ -262,48 +282,39 @@ template <> struct Fill<kC2R4> {
     const bool live = ok && t < nvalid;  // dead rows: S = Z = 0 gives exact zeros
     __bf16* row = tile + l * kRow;
     if (u < 32) {
-      const int v = u >> 3, q = u & 7;
-      if (q == 0) {
-        szv = live ? sz[v >> 1] : 0u;
-        const unsigned w = c[v];
-        // byte k of (w >> 2j) & 0x03030303 holds element 4k + j
-        b0 = mask_bytes(w, 0x03030303u);
-        b1 = mask_bytes(w >> 2, 0x03030303u);
-        b2 = mask_bytes(w >> 4, 0x03030303u);
-        b3 = mask_bytes(w >> 6, 0x03030303u);
+      // step 2 i + h of dword v: elements 2i, 2i + 1 (h = 0) or 8 + 2i, 8 + 2i + 1
+      // (h = 1), the low and high halves of the same two masked words: element
+      // j < 4 of a half sits at bit 2 j of the dword, element j >= 4 at bit
+      // 2 (j - 4) of the dword shifted by 8 (scale j % 4)
+      const int v = u >> 3, i = (u & 7) >> 1, h = u & 1;
+      if (h == 0) {
+        if ((u & 7) == 0 && (v & 1) == 0) zs = sz_scaled<4, 2>(live ? sz[v >> 1] : 0u);
+        const unsigned w = i < 2 ? c[v] : c[v] >> 8;
+        ma = mask_bytes(w, 0x00030003u << (2 * ((2 * i) & 3)));
+        mb = mask_bytes(w, 0x00030003u << (2 * ((2 * i + 1) & 3)));
       }
-      // elements 2q, 2q + 1 = byte k = q / 2 of b0, b1 (q even) or b2, b3 (q
-      // odd); the bytes 2 (q / 4), 2 (q / 4) + 1 of all four are converted at
-      // q % 4 = 0 (b0, b1) and 1 (b2, b3) and serve pairs q and q + 2
-      const int k = q >> 1;
-      if ((q & 3) == 0) {
-        f0 = code_pair_h(b0, q >> 2);
-        f1 = code_pair_h(b1, q >> 2);
+      const float ea = dq_sub(as_h2(ma)[h], zs.s[(2 * i) & 3], zs.sz);
+      const float eb = dq_sub(as_h2(mb)[h], zs.s[(2 * i + 1) & 3], zs.sz);
+      (h ? outh : outl)[i] = pack_bf16x2(ea, eb);
+      if ((u & 7) == 7) {
+        *(u32x4*)(row + 8 * (8 * cs + 2 * v)) = (u32x4){outl[0], outl[1], outl[2], outl[3]};
+        *(u32x4*)(row + 8 * (8 * cs + 2 * v + 1)) = (u32x4){outh[0], outh[1], outh[2], outh[3]};
       }
-      if ((q & 3) == 1) {
-        f2 = code_pair_h(b2, q >> 2);
-        f3 = code_pair_h(b3, q >> 2);
-      }
-      const float ea = dq_h((q & 1) ? f2[k & 1] : f0[k & 1], szv);
-      const float eb = dq_h((q & 1) ? f3[k & 1] : f1[k & 1], szv);
-      outw[q & 3] = pack_bf16x2(ea, eb);
-      if ((q & 3) == 3)
-        *(u32x4*)(row + 8 * (8 * cs + 2 * v + (q >> 2))) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
     } else {
-      const int q = u - 32;
+      // RoPE dword, 4-bit codes, split as dq_int4x8 does: pair q = elements
+      // 2q, 2q + 1 = half q / 2 of (ma, mb) (q even) or (mc, md)
+      const int q = u - 32, hf = q >> 1;
       if (q == 0) {
-        szv = live ? rsz : 0u;
-        b0 = mask_bytes(r, 0x0F0F0F0Fu);
-        b1 = mask_bytes(r >> 4, 0x0F0F0F0Fu);
+        zs = sz_scaled<4, 2>(live ? rsz : 0u);
+        ma = mask_bytes(r, 0x000F000Fu);
+        mb = mask_bytes(r, 0x00F000F0u);
+        mc = mask_bytes(r >> 8, 0x000F000Fu);
+        md = mask_bytes(r >> 8, 0x00F000F0u);
       }
-      if ((q & 1) == 0) {
-        f0 = code_pair_h(b0, q >> 1);
-        f1 = code_pair_h(b1, q >> 1);
-      }
-      const float ea = dq_h(f0[q & 1], szv);
-      const float eb = dq_h(f1[q & 1], szv);
-      outw[q] = pack_bf16x2(ea, eb);
-      if (q == 3) *(u32x4*)(row + 8 * (64 + cs)) = (u32x4){outw[0], outw[1], outw[2], outw[3]};
+      const float ea = dq_sub(as_h2((q & 1) ? mc : ma)[hf], zs.s[0], zs.sz);
+      const float eb = dq_sub(as_h2((q & 1) ? md : mb)[hf], zs.s[2], zs.sz);
+      outl[q] = pack_bf16x2(ea, eb);
+      if (q == 3) *(u32x4*)(row + 8 * (64 + cs)) = (u32x4){outl[0], outl[1], outl[2], outl[3]};
     }
   }
   __device__ __forceinline__ void store(__bf16* tile, int nvalid) {
@@ -952,20 +963,25 @@ __device__ __forceinline__ float lane_xor(float v, int m) {
   return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), m));
 }
 
-// 8 INT4 codes of a dword (element e in bits 4 e) -> bf16(fma(code, S, Z)),
-// (S, Z) the packed fp16 pair `sz`
-__device__ __forceinline__ bf16x8 dq_int4x8(unsigned w, unsigned sz) {
-  const unsigned lo = mask_bytes(w, 0x0F0F0F0Fu);       // elements 0, 2, 4, 6
-  const unsigned hi = mask_bytes(w >> 4, 0x0F0F0F0Fu);  // elements 1, 3, 5, 7
-  const h2 l0 = code_pair_h(lo, 0), l1 = code_pair_h(lo, 1), h0 = code_pair_h(hi, 0), h1 = code_pair_h(hi, 1);
-  const u32x4 o = {pack_bf16x2(dq_h(l0[0], sz), dq_h(h0[0], sz)), pack_bf16x2(dq_h(l0[1], sz), dq_h(h0[1], sz)),
-                   pack_bf16x2(dq_h(l1[0], sz), dq_h(h1[0], sz)), pack_bf16x2(dq_h(l1[1], sz), dq_h(h1[1], sz))};
+// 8 INT4 codes of a dword (element e in bits 4 e) -> bf16(fma(code, S, Z));
+// s24 = 2^24 S, s20 = 2^20 S, Z the high half of `sz`.  Elements 0, 4 sit at
+// bits 0, 16 (against s24), 1, 5 at bits 4, 20 (s20); 2, 6 and 3, 7 likewise
+// after a shift by 8.
+__device__ __forceinline__ bf16x8 dq_int4x8(unsigned w, float s24, float s20, unsigned sz) {
+  const h2 a = as_h2(mask_bytes(w, 0x000F000Fu)), b = as_h2(mask_bytes(w, 0x00F000F0u));
+  const unsigned w8 = w >> 8;
+  const h2 c = as_h2(mask_bytes(w8, 0x000F000Fu)), d = as_h2(mask_bytes(w8, 0x00F000F0u));
+  const u32x4 o = {pack_bf16x2(dq_sub(a[0], s24, sz), dq_sub(b[0], s20, sz)),
+                   pack_bf16x2(dq_sub(c[0], s24, sz), dq_sub(d[0], s20, sz)),
+                   pack_bf16x2(dq_sub(a[1], s24, sz), dq_sub(b[1], s20, sz)),
+                   pack_bf16x2(dq_sub(c[1], s24, sz), dq_sub(d[1], s20, sz))};
   return __builtin_bit_cast(bf16x8, o);
 }
-__device__ __forceinline__ bf16x8 dq_int2x8(const unsigned (&b)[4], int hf, unsigned sz) {
-  const h2 f0 = code_pair_h(b[0], hf), f1 = code_pair_h(b[1], hf), f2 = code_pair_h(b[2], hf), f3 = code_pair_h(b[3], hf);
-  const u32x4 o = {pack_bf16x2(dq_h(f0[0], sz), dq_h(f1[0], sz)), pack_bf16x2(dq_h(f2[0], sz), dq_h(f3[0], sz)),
-                   pack_bf16x2(dq_h(f0[1], sz), dq_h(f1[1], sz)), pack_bf16x2(dq_h(f2[1], sz), dq_h(f3[1], sz))};
+__device__ __forceinline__ bf16x8 dq_int2x8(const unsigned (&m)[8], int hf, const SzScaled<4>& z) {
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = dq_sub(as_h2(m[j])[hf], z.s[j % 4], z.sz);
+  const u32x4 o = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
   return __builtin_bit_cast(bf16x8, o);
 }
 
@@ -1022,11 +1038,12 @@ template <> struct SubFill<kC4R4> {
       rsz = __builtin_amdgcn_raw_buffer_load_b32(pg, o.rsz, Lay::kSzD + 64 * hp, 0);
     }
   }
-  __device__ __forceinline__ unsigned sz_of(int ks, bool live) const {
-    return live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u;
+  using Sz = SzScaled<2>;
+  __device__ __forceinline__ Sz sz_of(int ks, bool live) const {
+    return sz_scaled<2, 4>(live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u);
   }
-  __device__ __forceinline__ bf16x8 step(int ks, unsigned sz) {
-    return dq_int4x8(ks < 16 ? c[ks >> 2][ks & 3] : r[ks - 16], sz);
+  __device__ __forceinline__ bf16x8 step(int ks, const Sz& z) {
+    return dq_int4x8(ks < 16 ? c[ks >> 2][ks & 3] : r[ks - 16], z.s[0], z.s[1], z.sz);
   }
 };
 
@@ -1041,7 +1058,7 @@ template <> struct SubFill<kC2R4> {
   unsigned sz[4];
   unsigned r[2];
   unsigned rsz;
-  unsigned b[4];    // masked code bytes of the dword being converted
+  unsigned m[8];    // the dword being converted, split as int2_split does
   __device__ __forceinline__ void issue(int i, __amdgpu_buffer_rsrc_t pg, int hp, const SubLanes& o) {
     if (i < 4) {
       c[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(pg, o.c, Lay::kCodesA + 256 * hp + 2048 * i, 0));
@@ -1053,18 +1070,15 @@ template <> struct SubFill<kC2R4> {
       rsz = __builtin_amdgcn_raw_buffer_load_b32(pg, o.rsz, Lay::kSzD + 64 * hp, 0);
     }
   }
-  __device__ __forceinline__ unsigned sz_of(int ks, bool live) const {
-    return live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u;
+  using Sz = SzScaled<4>;   // 2^24 S, 2^22 S, 2^20 S, 2^18 S (the RoPE codes use 2^24 S and 2^20 S)
+  __device__ __forceinline__ Sz sz_of(int ks, bool live) const {
+    return sz_scaled<4, 2>(live ? (ks < 16 ? sz[ks >> 2] : rsz) : 0u);
   }
   // k-step 4 m + d: half d & 1 of dword d / 2 of block m
-  __device__ __forceinline__ bf16x8 step(int ks, unsigned sz) {
-    if (ks >= 16) return dq_int4x8(r[ks - 16], sz);
-    if ((ks & 1) == 0) {
-      const unsigned w = c[ks >> 2][(ks & 3) >> 1];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = mask_bytes(w >> (2 * j), 0x03030303u);
-    }
-    return dq_int2x8(b, ks & 1, sz);
+  __device__ __forceinline__ bf16x8 step(int ks, const Sz& z) {
+    if (ks >= 16) return dq_int4x8(r[ks - 16], z.s[0], z.s[2], z.sz);
+    if ((ks & 1) == 0) int2_split(c[ks >> 2][(ks & 3) >> 1], m);
+    return dq_int2x8(m, ks & 1, z);
   }
 };
 
@@ -1170,7 +1184,7 @@ __device__ __forceinline__ bool iw_pass(const DecodeArgs& a, __bf16* smem, const
   bf16x8 qall[18];
 #pragma unroll
   for (int d = 0; d < 18; ++d) qall[d] = qg ? *(const bf16x8*)(qg + iw_chan(iw_ks(d), g)) : (bf16x8){};
-  unsigned SZ0 = 0u, SZ1 = 0u;  // (S, Z) fp16 pairs of the current group of each block
+  typename SF::Sz SZ0, SZ1;  // (S, Z) of the current group of each block
   bool live0 = false, live1 = false;
   auto qk_begin = [&](int u) {
     const bool ok = pg_next >= 0 && pg_next < a.num_pages;
