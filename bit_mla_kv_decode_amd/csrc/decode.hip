@@ -135,10 +135,11 @@ template <int N> struct SzScaled {
 };
 template <int N, int kBits>
 __device__ __forceinline__ SzScaled<N> sz_scaled(unsigned sz) {
-  const float S = (float)__builtin_bit_cast(h2, sz)[0];
+  const _Float16 S = __builtin_bit_cast(h2, sz)[0];
   SzScaled<N> r;
+  // one v_fma_mix_f32 each (S >= 0, so adding +0 changes nothing)
 #pragma unroll
-  for (int i = 0; i < N; ++i) r.s[i] = S * (float)(1 << (24 - kBits * i));
+  for (int i = 0; i < N; ++i) r.s[i] = __builtin_fmaf((float)S, (float)(1 << (24 - kBits * i)), 0.0f);
   r.sz = sz;
   return r;
 }
