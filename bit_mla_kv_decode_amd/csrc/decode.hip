@@ -932,8 +932,8 @@ __device__ __forceinline__ void write_split(const DecodeArgs& a, int b, int64_t 
 //      in its lane (channels iw_chan(ks, g) .. + 8) are one code dword;
 //   2. dequantizes k-step by k-step in registers, straight into the A operand
 //      of MFMA 16x16x32 bf16 (16 tokens x 32 channels), one MFMA per block
-//      sharing B = q^T (the rows of the piece are staged in LDS once per
-//      piece and held in registers for the pass); the content values also go
+//      sharing B = q^T (the rows of the piece are loaded from global memory
+//      once per pass and held in registers); the content values also go
 //      to the wavefront's own LDS buffer for step 4.  Output: S^T, lane (h, g) holding row h for tokens
 //      4 g .. 4 g + 3 of each block;
 //   3. takes the eight softmax weights of its lane against a fixed reference
@@ -1558,8 +1558,7 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
 
 // Per-sequence splits: workgroup (split, b) covers pages [split * P, (split + 1) * P)
 // of sequence b, the last split running to the end of the sequence.
-// Threads of a decode workgroup: 512 for the independent-wavefront variant
-// (C = 0), else 256.
+// Threads of a decode workgroup: 256 (four wavefronts) in every variant.
 template <int C> constexpr int decode_threads() { return C == 0 ? kIwThreads : kThreads; }
 
 template <int F, bool kDirect, int C>
@@ -1895,7 +1894,7 @@ __global__ __launch_bounds__(256) void k_combine_flat(const float* __restrict__ 
 constexpr size_t kDecodeLds = (2 * (size_t)kTile + 128 * kQRow) * sizeof(__bf16);  // 142336 bytes
 template <int C> constexpr size_t decode_lds() {
   // channel split: two tiles and 4 KB of weights per head group (4 / C groups);
-  // independent wavefronts: eight V buffers, q and the merge record
+  // independent wavefronts: four V buffers and the merge record
   return C == 0 ? kIwLds : C > 1 ? 2 * (size_t)kTile * sizeof(__bf16) + 4096 * (4 / C) : kDecodeLds;
 }
 
