@@ -1811,6 +1811,18 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ o_part, c
   // a sequence has at most kCombineMaxSlots pieces; the clamp only keeps LDS
   // accesses in bounds for a workspace the decode did not write
   count = count < kCombineMaxSlots ? count : kCombineMaxSlots;
+  const int ch = 64 * NC * part + NC * lane;
+  const float* base = o_part + (first * H + head) * kDc + ch;
+  // with one channel per lane and at most kPre slots, every row is loaded
+  // before the weights are known, so the merge waits for memory once (rows
+  // of zero weight are then read but not added)
+  constexpr int kPre = NC == 1 ? 48 : 1;
+  const bool pre = NC == 1 && count <= kPre;
+  float xp[kPre];
+  if (pre) {
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) xp[j] = j < count ? base[(int64_t)j * H * kDc] : 0.0f;
+  }
   // slot s's log-sum-exp in lane s % 64; the first 64 stay in a register
   const float ls0 = lane < count ? lse_part[(first + lane) * H + head] : -INFINITY;
   float M = ls0;
@@ -1830,10 +1842,14 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ o_part, c
     }
     W = wave_sum(W);
   }
-  const int ch = 64 * NC * part + NC * lane;
   vec acc = {};
-  if (M != -INFINITY) {
-    const float* base = o_part + (first * H + head) * kDc + ch;
+  if (M != -INFINITY && pre) {
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const float w = j < count ? wbuf[j] : 0.0f;
+      acc[0] += w > 0.0f ? w * xp[j] : 0.0f;
+    }
+  } else if (M != -INFINITY) {
     for (int s0 = 0; s0 < count; s0 += U) {
       float w[U];
       vec x[U];
