@@ -416,3 +416,32 @@ def test_multi_token_single_query_equals_decode():
         o2, _ = mla.mla_decode_multi_lowbit(fmt, q.cuda()[:, None].contiguous(), cache, btd, sld, SCALE, num_splits=S)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2[:, 0])
+
+
+@pytest.mark.parametrize("fmt,heads,splits", [("C4R4", 16, 0), ("C2R4", 24, 0), ("C4R4", 48, 2), ("C2R4", 128, 0),
+                                              ("BF16", 128, 0)])
+def test_large_batch(fmt, heads, splits):
+    """700 short ragged sequences (empty, single-token, partial-tile, up to a
+    few pages): more sequences than the balanced partition has workgroups, so
+    shares hold many pieces; the walk reads lengths beyond the first 256 from
+    global memory and crosses many 64-sequence chunks; the combine merges
+    every sequence's slots."""
+    B = 700
+    _say("large batch %s H=%d S=%d B=%d" % (fmt, heads, splits, B))
+    rng = np.random.default_rng(heads + 31 * splits)
+    kind = rng.integers(0, 10, size=B)
+    lens = np.where(kind == 0, 0, np.where(kind == 1, 1, np.where(kind < 5, rng.integers(2, 64, size=B),
+                                                                   rng.integers(64, 400, size=B)))).astype(np.int32)
+    w = W.Workload("batch", fmt, batch=B, heads=heads, outliers=fmt == "C2R4", pages="random", seed=heads)
+    bt, npages = W.page_table(w, lens, 2)
+    cache = mla.alloc_cache(fmt, npages)
+    for b, L in enumerate(lens):
+        if L:
+            lat, rope = W.sequence_rows(w, b, 0, int(L), "cuda")
+            mla.mla_quant_append(fmt, lat, rope, torch.from_numpy(W.slots_for(bt, b, 0, int(L))).cuda(), cache)
+    q = W.queries(w, "cpu")
+    out, lse = gpu_decode(fmt, q, cache, bt, lens, splits)
+    ref, ref_lse = oracle.decode(OFMT[fmt], q, cache.cpu().numpy(), npages, bt, lens, SCALE)
+    assert_close(out, ref, "%s H=%d B=%d" % (fmt, heads, B))
+    assert_lse(lse, ref_lse)
+    assert (out[lens == 0] == 0).all()
