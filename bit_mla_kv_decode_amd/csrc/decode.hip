@@ -870,14 +870,21 @@ __device__ __forceinline__ void write_split_cs(const DecodeArgs& a, int b, int64
   } else {
     const int64_t prow = slot * R + head;
     float* orow = a.o_part + prow * kDc + 4 * hi + 32 * (part * NCT);
+    // the four stores of a channel tile fill its 128-byte lines of the 32
+    // rows: kept together (the fences stop the scheduler from interleaving
+    // the tiles), a line is complete before the write burst at the end of
+    // the kernel can evict it half written, which doubled the bytes written
+    // to HBM at 64 heads
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const f32x4 v = {acc.o[ct][4 * rq] * inv, acc.o[ct][4 * rq + 1] * inv, acc.o[ct][4 * rq + 2] * inv,
                          acc.o[ct][4 * rq + 3] * inv};
         *(f32x4*)(orow + 32 * ct + 8 * rq) = v;
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (hi == 0 && part == 0) a.lse_part[prow] = lse;
   }
 }
